@@ -1,0 +1,193 @@
+/*
+ * pa.h -- C ABI of the MI355X (gfx950) paged-KV hot path.
+ *
+ * Two operations, as the LLM stack book "4.6 PagedAttention & KV-Cache Memory
+ * Management" states the problem (sections "Block Tables, the Allocator &
+ * Copy-on-Write", "The PagedAttention Kernel", "From Python bookkeeping to the
+ * tensors the kernel actually takes"):
+ *
+ *   pa_write_kv  -- scatter each new token's K and V rows into the block pools at
+ *                   slot = physical_block * block_size + offset;
+ *   pa_decode    -- attention of one query token per sequence over its cached
+ *                   tokens, softmax(scale * q . K^T) V, gathering K and V through
+ *                   the sequence's block table, with grouped-query heads.
+ *
+ * pa_decode runs in two stages that are also exported on their own:
+ * pa_decode_partition (per-partition softmax pieces, split-K over the sequence:
+ * "Performance considerations") and pa_merge (combines the pieces).
+ *
+ * Conventions for every call:
+ *   - Pointers named as device data are device pointers (hipMalloc / torch CUDA
+ *     tensors) owned by the caller; arrays are row-major and contiguous.  The
+ *     library never allocates, frees or keeps device memory, and keeps no
+ *     state between calls; calls are thread-safe.
+ *   - `stream` is a hipStream_t (NULL = the null stream).  Calls only enqueue
+ *     work: no host synchronization, no allocation, so they can be captured in
+ *     a HIP graph.
+ *   - A host-checkable contract violation returns a nonzero pa_status before
+ *     anything is enqueued and leaves all outputs untouched.  A failed launch
+ *     returns PA_ERR_HIP.
+ *   - Invalid *data* is undefined behaviour: a slot or block id outside the
+ *     pool, context_lens[b] > max_blocks_per_seq * block_size, duplicate slots
+ *     in one write, or an `out` that aliases an input.
+ *
+ * Pool layout (both pools, same shape and format):
+ *   [num_blocks, block_size, num_kv_heads, head_dim]
+ * (LLM stack book, "Block Tables, the Allocator & Copy-on-Write"; ai-infra-
+ * handbooks "Paged KV cache", section "Implementation").  Viewed as
+ * [num_blocks * block_size, num_kv_heads * head_dim] it is slot-major.
+ */
+#ifndef PA_H_
+#define PA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum pa_status {
+  PA_OK = 0,
+  PA_ERR_NULL = 1,        /* a required pointer is NULL */
+  PA_ERR_SHAPE = 2,       /* inconsistent or out-of-range sizes */
+  PA_ERR_DTYPE = 3,       /* unsupported dtype or dtype combination */
+  PA_ERR_UNSUPPORTED = 4, /* supported dtypes, unsupported head_dim / block_size / partition size */
+  PA_ERR_WORKSPACE = 5,   /* workspace missing or smaller than pa_decode_workspace_bytes() */
+  PA_ERR_HIP = 6          /* the HIP runtime reported an error when launching */
+} pa_status;
+
+typedef enum pa_dtype {
+  PA_F32 = 0,             /* IEEE binary32 */
+  PA_BF16 = 1,            /* bfloat16: the upper 16 bits of a binary32 */
+  PA_FP8_E4M3 = 2         /* OCP E4M3FN (bias 7, no infinity, S.1111.111 = NaN, max 448) */
+} pa_dtype;
+
+/* Describes both pools.  k_scale / v_scale are used only for PA_FP8_E4M3
+ * pools: the real value of a stored code c is e4m3(c) * scale (one fp32 scale
+ * per pool).  The pages only say an fp8 cache halves the bytes per element
+ * (LLM stack book, "The libraries that implement this"); the per-tensor scale
+ * is this library's reading of it. */
+typedef struct pa_kv_cache {
+  int64_t num_blocks;     /* physical blocks in each pool, >= 1 */
+  int32_t block_size;     /* tokens per block: a power of two, 1..1024 */
+  int32_t num_kv_heads;   /* H_kv >= 1 */
+  int32_t head_dim;       /* d_h: 64 or 128 */
+  int32_t dtype;          /* pa_dtype of the pool elements */
+  float k_scale;          /* fp8 pools: > 0 and finite */
+  float v_scale;
+} pa_kv_cache;
+
+/* Slot-mapping write (reshape-and-cache).
+ *
+ * For every token i < num_tokens with s = slot_mapping[i] >= 0, copies row
+ * k[i] (num_kv_heads * head_dim elements) to k_cache block s / block_size,
+ * offset s % block_size, and likewise v[i] to v_cache (LLM stack book, "From
+ * Python bookkeeping ...": the write is one indexed copy into the pool seen as
+ * [num_blocks * block_size, H_kv, d_h]; "Putting It Together": divmod of the
+ * slot).  A negative slot skips the token (padding).
+ *
+ *   k, v          device, [num_tokens, num_kv_heads, head_dim] of in_dtype
+ *   in_dtype      == cache->dtype for PA_F32 / PA_BF16 pools (bit-exact copy);
+ *                 PA_BF16 or PA_F32 for a PA_FP8_E4M3 pool, which stores
+ *                 RNE-saturating e4m3(fp32(x * fp32(1 / scale))), NaN -> NaN
+ *                 code with the input's sign
+ *   slot_mapping  device int32 [num_tokens]; slots must be distinct and
+ *                 < num_blocks * block_size
+ *   k_cache, v_cache  device pools, written in place
+ * Errors: PA_ERR_NULL, PA_ERR_SHAPE (num_tokens < 0, num_blocks * block_size
+ * beyond int32 slots), PA_ERR_DTYPE, PA_ERR_UNSUPPORTED, PA_ERR_HIP.
+ * num_tokens == 0 is a no-op returning PA_OK. */
+pa_status pa_write_kv(const void* k, const void* v, int32_t in_dtype, int32_t num_tokens,
+                      const int32_t* slot_mapping, void* k_cache, void* v_cache,
+                      const pa_kv_cache* cache, void* stream);
+
+/* Partition size (tokens) used when a call passes partition_tokens = 0. */
+int32_t pa_default_partition_tokens(void);
+
+/* Workspace bytes pa_decode / pa_decode_partition / pa_merge need for this shape
+ * (0 when max_context_len fits in one partition).  partition_tokens = 0 means
+ * the default.  Layout, each region aligned to 256 bytes:
+ *   m [num_seqs, num_q_heads, J] f32, l [num_seqs, num_q_heads, J] f32,
+ *   o [num_seqs, num_q_heads, J, head_dim] f32,  J = ceil(max_context_len / P).
+ * Returns 0 for invalid arguments. */
+size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                                 int32_t max_context_len, int32_t partition_tokens);
+
+/* Kernel selection for pa_decode / pa_decode_partition. */
+typedef enum pa_kernel {
+  PA_KERNEL_AUTO = 0,     /* matrix-core path for bf16/e4m3 pools, vector path for f32 */
+  PA_KERNEL_VALU = 1,     /* vector-ALU path (all formats, query-head group <= 8) */
+  PA_KERNEL_MFMA = 2      /* matrix-core path (bf16 q with bf16 or e4m3 pools, group <= 16) */
+} pa_kernel;
+
+/* Paged decode attention for one new token per sequence.
+ *
+ * out[b, h, :] = softmax_t(scale * q[b, h, :] . K[b, t, kvh, :]) V[b, t, kvh, :]
+ * over t < context_lens[b], with kvh = h / (num_q_heads / num_kv_heads) (query
+ * heads grouped contiguously, LLM stack book "The PagedAttention Kernel") and
+ * token t read from physical block block_tables[b, t / block_size] at offset
+ * t % block_size (mohdvasim.com "PagedAttention - Explained", "The Custom CUDA
+ * Kernel Overview").  A sequence with context_lens[b] == 0 gets zeros.
+ *
+ *   q             device [num_seqs, num_q_heads, head_dim] of q_dtype
+ *                 (PA_F32 with an f32 pool; PA_BF16 with a bf16 or e4m3 pool)
+ *   k_cache, v_cache, cache   the pools (read only)
+ *   block_tables  device int32 [num_seqs, max_blocks_per_seq]; entries at index
+ *                 >= ceil(context_lens[b] / block_size) are never read
+ *   context_lens  device int32 [num_seqs]: tokens valid after this step's write,
+ *                 0 <= context_lens[b] <= max_context_len
+ *   max_context_len  host-known bound on context_lens (sizes the grid, so no
+ *                 device-to-host copy is needed); <= max_blocks_per_seq * block_size
+ *   scale         softmax scale (1/sqrt(head_dim) for standard attention), finite
+ *   out           device [num_seqs, num_q_heads, head_dim] of q_dtype
+ *   workspace     device scratch of >= pa_decode_workspace_bytes(...) bytes
+ *                 (may be NULL when that is 0); contents are overwritten
+ *   partition_tokens  16, 32, 64, 128 or 256 (0 = default).  Results do not
+ *                 depend on block_size or on where blocks sit in the pool: the
+ *                 reduction order is fixed by logical token positions.
+ *   kernel        pa_kernel
+ * Outputs are bf16-rounded (nearest even) for bf16 q.  The matrix-core path
+ * rounds the softmax probabilities to bf16 before P.V (and sums the same
+ * rounded values in the denominator).
+ * Errors: PA_ERR_NULL, PA_ERR_SHAPE, PA_ERR_DTYPE, PA_ERR_UNSUPPORTED,
+ * PA_ERR_WORKSPACE, PA_ERR_HIP.  num_seqs == 0 is a no-op returning PA_OK. */
+pa_status pa_decode(const void* q, int32_t q_dtype, int32_t num_seqs, int32_t num_q_heads,
+                    const void* k_cache, const void* v_cache, const pa_kv_cache* cache,
+                    const int32_t* block_tables, int32_t max_blocks_per_seq,
+                    const int32_t* context_lens, int32_t max_context_len, float scale,
+                    void* out, void* workspace, size_t workspace_bytes,
+                    int32_t partition_tokens, int32_t kernel, void* stream);
+
+/* First stage of pa_decode alone (same arguments and checks).  For every
+ * sequence with context_lens[b] <= P it writes out[b] directly; for longer
+ * sequences it writes partition j's pieces into the workspace, with
+ * x_t = scale * q . K_t * log2(e):
+ *   m_j = max x_t,  l_j = sum 2^(x_t - m_j),  o_j = sum 2^(x_t - m_j) V_t
+ * over the partition's tokens [j*P, min((j+1)*P, ctx)). */
+pa_status pa_decode_partition(const void* q, int32_t q_dtype, int32_t num_seqs, int32_t num_q_heads,
+                              const void* k_cache, const void* v_cache, const pa_kv_cache* cache,
+                              const int32_t* block_tables, int32_t max_blocks_per_seq,
+                              const int32_t* context_lens, int32_t max_context_len, float scale,
+                              void* out, void* workspace, size_t workspace_bytes,
+                              int32_t partition_tokens, int32_t kernel, void* stream);
+
+/* Second stage of pa_decode: for every sequence with n = ceil(context_lens[b] / P)
+ * >= 2 partitions and every query head,
+ *   out = sum_j 2^(m_j - M) o_j / sum_j 2^(m_j - M) l_j,   M = max_j m_j,
+ * over j < n, reading the workspace layout above.  Sequences with n <= 1 are
+ * left untouched.  out_dtype is PA_F32 or PA_BF16; head_dim is 64 or 128.
+ * Errors: PA_ERR_NULL, PA_ERR_SHAPE, PA_ERR_DTYPE, PA_ERR_UNSUPPORTED,
+ * PA_ERR_WORKSPACE, PA_ERR_HIP. */
+pa_status pa_merge(const void* workspace, size_t workspace_bytes, int32_t num_seqs, int32_t num_q_heads,
+                   int32_t head_dim, const int32_t* context_lens, int32_t max_context_len,
+                   int32_t partition_tokens, int32_t out_dtype, void* out, void* stream);
+
+/* Static, human-readable name of a status code. */
+const char* pa_status_str(pa_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H_ */

@@ -1,0 +1,241 @@
+"""ctypes binding of ``libpa.so`` (the C ABI in ``include/pa.h``).
+
+Argument marshalling only: every step of the paged-KV path runs in the HIP
+library.  torch is used for device pointers and the current stream, never for
+the computation.  The library is loaded on first use; if it has not been built
+the first call raises, it never falls back to anything else.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libpa.so")
+
+# pa_status
+PA_OK, PA_ERR_NULL, PA_ERR_SHAPE, PA_ERR_DTYPE, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_HIP = range(7)
+# pa_dtype
+PA_F32, PA_BF16, PA_FP8_E4M3 = 0, 1, 2
+# pa_kernel
+PA_KERNEL_AUTO, PA_KERNEL_VALU, PA_KERNEL_MFMA = 0, 1, 2
+
+EXPORTED = ("pa_write_kv", "pa_decode", "pa_decode_partition", "pa_merge", "pa_decode_workspace_bytes",
+            "pa_default_partition_tokens", "pa_status_str")
+
+
+class PaKvCache(ctypes.Structure):
+    """struct pa_kv_cache"""
+    _fields_ = [("num_blocks", ctypes.c_int64), ("block_size", ctypes.c_int32),
+                ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("dtype", ctypes.c_int32), ("k_scale", ctypes.c_float), ("v_scale", ctypes.c_float)]
+
+
+class PaError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(msg)
+        self.status = status
+
+
+_lib = None
+_vp, _i32, _i64, _f32, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+_DECODE_ARGS = [_vp, _i32, _i32, _i32, _vp, _vp, ctypes.POINTER(PaKvCache), _vp, _i32, _vp, _i32, _f32,
+                _vp, _vp, _sz, _i32, _i32, _vp]
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library; raises if ``libpa.so`` has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"HIP library not built: {LIB_PATH} is missing "
+                               "(run __graft_entry__.build() or python paged_kv_cache_112_amd/build.py)")
+        L = ctypes.CDLL(LIB_PATH)
+        L.pa_write_kv.argtypes = [_vp, _vp, _i32, _i32, _vp, _vp, _vp, ctypes.POINTER(PaKvCache), _vp]
+        L.pa_write_kv.restype = ctypes.c_int
+        L.pa_decode.argtypes = _DECODE_ARGS
+        L.pa_decode.restype = ctypes.c_int
+        L.pa_decode_partition.argtypes = _DECODE_ARGS
+        L.pa_decode_partition.restype = ctypes.c_int
+        L.pa_merge.argtypes = [_vp, _sz, _i32, _i32, _i32, _vp, _i32, _i32, _i32, _vp, _vp]
+        L.pa_merge.restype = ctypes.c_int
+        L.pa_decode_workspace_bytes.argtypes = [_i32, _i32, _i32, _i32, _i32]
+        L.pa_decode_workspace_bytes.restype = _sz
+        L.pa_default_partition_tokens.argtypes = []
+        L.pa_default_partition_tokens.restype = _i32
+        L.pa_status_str.argtypes = [ctypes.c_int]
+        L.pa_status_str.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def status_str(status: int) -> str:
+    return lib().pa_status_str(status).decode()
+
+
+def check(status: int) -> None:
+    if status != PA_OK:
+        raise PaError(status, status_str(status))
+
+
+# ---------------------------------------------------------------------------
+# raw C entry points (same names as the C ABI; plain integers and addresses)
+# ---------------------------------------------------------------------------
+def pa_write_kv(k, v, in_dtype, num_tokens, slot_mapping, k_cache, v_cache, cache: PaKvCache, stream) -> int:
+    return lib().pa_write_kv(k, v, in_dtype, num_tokens, slot_mapping, k_cache, v_cache, ctypes.byref(cache), stream)
+
+
+def pa_decode(q, q_dtype, num_seqs, num_q_heads, k_cache, v_cache, cache: PaKvCache, block_tables,
+              max_blocks_per_seq, context_lens, max_context_len, scale, out, workspace, workspace_bytes,
+              partition_tokens=0, kernel=PA_KERNEL_AUTO, stream=None) -> int:
+    return lib().pa_decode(q, q_dtype, num_seqs, num_q_heads, k_cache, v_cache, ctypes.byref(cache), block_tables,
+                           max_blocks_per_seq, context_lens, max_context_len, scale, out, workspace,
+                           workspace_bytes, partition_tokens, kernel, stream)
+
+
+def pa_decode_partition(q, q_dtype, num_seqs, num_q_heads, k_cache, v_cache, cache: PaKvCache, block_tables,
+                        max_blocks_per_seq, context_lens, max_context_len, scale, out, workspace, workspace_bytes,
+                        partition_tokens=0, kernel=PA_KERNEL_AUTO, stream=None) -> int:
+    return lib().pa_decode_partition(q, q_dtype, num_seqs, num_q_heads, k_cache, v_cache, ctypes.byref(cache),
+                                     block_tables, max_blocks_per_seq, context_lens, max_context_len, scale, out,
+                                     workspace, workspace_bytes, partition_tokens, kernel, stream)
+
+
+def pa_merge(workspace, workspace_bytes, num_seqs, num_q_heads, head_dim, context_lens, max_context_len,
+             partition_tokens, out_dtype, out, stream=None) -> int:
+    return lib().pa_merge(workspace, workspace_bytes, num_seqs, num_q_heads, head_dim, context_lens,
+                          max_context_len, partition_tokens, out_dtype, out, stream)
+
+
+def pa_decode_workspace_bytes(num_seqs, num_q_heads, head_dim, max_context_len, partition_tokens=0) -> int:
+    return lib().pa_decode_workspace_bytes(num_seqs, num_q_heads, head_dim, max_context_len, partition_tokens)
+
+
+def pa_default_partition_tokens() -> int:
+    return lib().pa_default_partition_tokens()
+
+
+# ---------------------------------------------------------------------------
+# torch conveniences: tensors in, same calls
+# ---------------------------------------------------------------------------
+def _torch():
+    import torch
+    return torch
+
+
+def dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return PA_F32
+    if t.dtype == torch.bfloat16:
+        return PA_BF16
+    if t.dtype in (torch.uint8, getattr(torch, "float8_e4m3fn", torch.uint8)):
+        return PA_FP8_E4M3
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _ptr(t) -> int:
+    if not t.is_cuda:
+        raise ValueError("expected a device tensor")
+    if not t.is_contiguous():
+        raise ValueError("expected a contiguous tensor")
+    return t.data_ptr()
+
+
+def _stream(stream) -> int:
+    if stream is not None:
+        return int(stream)
+    return _torch().cuda.current_stream().cuda_stream
+
+
+def cache_desc(k_cache, k_scale: float = 1.0, v_scale: float = 1.0) -> PaKvCache:
+    nb, bs, hkv, d = k_cache.shape
+    return PaKvCache(nb, bs, hkv, d, dtype_code(k_cache), float(k_scale), float(v_scale))
+
+
+def write_kv(k, v, slot_mapping, k_cache, v_cache, k_scale: float = 1.0, v_scale: float = 1.0, stream=None) -> None:
+    """pa_write_kv on torch tensors: k, v [N, H_kv, d]; slot_mapping int32 [N]; pools [nb, bs, H_kv, d]."""
+    if k_cache.shape != v_cache.shape or k_cache.dtype != v_cache.dtype:
+        raise ValueError("K and V pools must match")
+    if k.shape != v.shape or k.dim() != 3 or k.shape[1:] != k_cache.shape[2:]:
+        raise ValueError("k/v must be [N, H_kv, head_dim] matching the pools")
+    if slot_mapping.dtype != _torch().int32 or slot_mapping.numel() != k.shape[0]:
+        raise ValueError("slot_mapping must be int32 [N]")
+    desc = cache_desc(k_cache, k_scale, v_scale)
+    check(pa_write_kv(_ptr(k), _ptr(v), dtype_code(k), k.shape[0], _ptr(slot_mapping), _ptr(k_cache),
+                      _ptr(v_cache), desc, _stream(stream)))
+
+
+def decode_workspace_bytes(num_seqs, num_q_heads, head_dim, max_context_len, partition_tokens=0) -> int:
+    return pa_decode_workspace_bytes(num_seqs, num_q_heads, head_dim, max_context_len, partition_tokens)
+
+
+def _decode_common(fn, q, k_cache, v_cache, block_tables, context_lens, scale, out, max_context_len, workspace,
+                   partition_tokens, kernel, k_scale, v_scale, stream):
+    torch = _torch()
+    B, hq, d = q.shape
+    if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
+        raise ValueError("block_tables and context_lens must be int32")
+    if block_tables.dim() != 2 or block_tables.shape[0] != B or context_lens.numel() != B:
+        raise ValueError("block_tables [B, max_blocks] and context_lens [B] must match q")
+    if k_cache.shape != v_cache.shape or k_cache.shape[3] != d:
+        raise ValueError("pools must match each other and q's head_dim")
+    bs = k_cache.shape[1]
+    if max_context_len is None:
+        max_context_len = block_tables.shape[1] * bs
+    if out is None:
+        out = torch.empty_like(q)
+    need = pa_decode_workspace_bytes(B, hq, d, max_context_len, partition_tokens)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = _ptr(workspace) if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    desc = cache_desc(k_cache, k_scale, v_scale)
+    check(fn(_ptr(q), dtype_code(q), B, hq, _ptr(k_cache), _ptr(v_cache), desc, _ptr(block_tables),
+             block_tables.shape[1], _ptr(context_lens), int(max_context_len), float(scale), _ptr(out), ws_ptr,
+             ws_bytes, int(partition_tokens), int(kernel), _stream(stream)))
+    return out, workspace
+
+
+def decode(q, k_cache, v_cache, block_tables, context_lens, scale, out=None, max_context_len=None, workspace=None,
+           partition_tokens=0, kernel=PA_KERNEL_AUTO, k_scale=1.0, v_scale=1.0, stream=None):
+    """pa_decode on torch tensors; returns ``out`` [B, H_q, d] in q's dtype.
+
+    ``max_context_len`` defaults to block_tables.shape[1] * block_size, so no
+    device-to-host copy is needed.  A workspace is allocated when none is given.
+    """
+    return _decode_common(pa_decode, q, k_cache, v_cache, block_tables, context_lens, scale, out, max_context_len,
+                          workspace, partition_tokens, kernel, k_scale, v_scale, stream)[0]
+
+
+def decode_partition(q, k_cache, v_cache, block_tables, context_lens, scale, out=None, max_context_len=None,
+                     workspace=None, partition_tokens=0, kernel=PA_KERNEL_AUTO, k_scale=1.0, v_scale=1.0,
+                     stream=None):
+    """pa_decode_partition on torch tensors; returns (out, workspace)."""
+    return _decode_common(pa_decode_partition, q, k_cache, v_cache, block_tables, context_lens, scale, out,
+                          max_context_len, workspace, partition_tokens, kernel, k_scale, v_scale, stream)
+
+
+def merge(workspace, context_lens, out, max_context_len, partition_tokens=0, stream=None):
+    """pa_merge on torch tensors (out [B, H_q, d], f32 or bf16)."""
+    B, hq, d = out.shape
+    ws_ptr = _ptr(workspace) if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    check(pa_merge(ws_ptr, ws_bytes, B, hq, d, _ptr(context_lens), int(max_context_len), int(partition_tokens),
+                   dtype_code(out), _ptr(out), _stream(stream)))
+    return out
+
+
+def workspace_views(workspace, num_seqs, num_q_heads, head_dim, max_context_len, partition_tokens=0):
+    """(m, l, o) float32 views of a workspace, following the layout in include/pa.h."""
+    P = partition_tokens or pa_default_partition_tokens()
+    J = 1 if max_context_len <= P else -(-max_context_len // P)
+    rows = num_seqs * num_q_heads * J
+    al = lambda x: (x + 255) // 256 * 256
+    f = workspace.view(_torch().uint8)
+    m = f[0:rows * 4].view(_torch().float32).view(num_seqs, num_q_heads, J)
+    l_off = al(rows * 4)
+    l = f[l_off:l_off + rows * 4].view(_torch().float32).view(num_seqs, num_q_heads, J)
+    o_off = l_off + al(rows * 4)
+    o = f[o_off:o_off + rows * head_dim * 4].view(_torch().float32).view(num_seqs, num_q_heads, J, head_dim)
+    return m, l, o

@@ -1,0 +1,278 @@
+// C ABI of the paged-KV library: argument checks, workspace sizing and kernel
+// dispatch.  Every check runs on the host before anything is enqueued.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "../../include/pa.h"
+#include "launch.hpp"
+
+namespace {
+
+constexpr int32_t kDefaultPartition = 256;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool is_pow2(int64_t x) { return x > 0 && (x & (x - 1)) == 0; }
+
+int32_t log2i(int64_t x) {
+  int32_t r = 0;
+  while ((int64_t(1) << r) < x) ++r;
+  return r;
+}
+
+int32_t elem_bytes(int32_t fmt) { return fmt == PA_F32 ? 4 : fmt == PA_BF16 ? 2 : 1; }
+
+bool valid_partition(int32_t p) { return p == 16 || p == 32 || p == 64 || p == 128 || p == 256; }
+
+struct Workspace {
+  size_t m_off, l_off, o_off, bytes;
+  int32_t parts;
+};
+
+// Returns false for invalid sizes.
+bool workspace_layout(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim, int32_t max_context_len,
+                      int32_t partition, Workspace* w) {
+  if (num_seqs < 0 || num_q_heads <= 0 || head_dim <= 0 || max_context_len < 0 || !valid_partition(partition))
+    return false;
+  const int64_t parts = max_context_len <= partition ? 1 : (max_context_len + partition - 1) / partition;
+  w->parts = (int32_t)parts;
+  if (parts <= 1) {
+    w->m_off = w->l_off = w->o_off = w->bytes = 0;
+    return true;
+  }
+  const size_t rows = (size_t)num_seqs * (size_t)num_q_heads * (size_t)parts;
+  w->m_off = 0;
+  w->l_off = align_up(rows * 4);
+  w->o_off = w->l_off + align_up(rows * 4);
+  w->bytes = w->o_off + align_up(rows * (size_t)head_dim * 4);
+  return true;
+}
+
+pa_status check_cache(const pa_kv_cache* c) {
+  if (!c) return PA_ERR_NULL;
+  if (c->num_blocks < 1 || c->num_kv_heads < 1 || c->block_size < 1) return PA_ERR_SHAPE;
+  if (c->dtype != PA_F32 && c->dtype != PA_BF16 && c->dtype != PA_FP8_E4M3) return PA_ERR_DTYPE;
+  if (!is_pow2(c->block_size) || c->block_size > 1024) return PA_ERR_UNSUPPORTED;
+  if (c->head_dim != 64 && c->head_dim != 128) return PA_ERR_UNSUPPORTED;
+  if (c->dtype == PA_FP8_E4M3) {
+    if (!(c->k_scale > 0.f) || !(c->v_scale > 0.f) || !std::isfinite(c->k_scale) || !std::isfinite(c->v_scale))
+      return PA_ERR_SHAPE;
+  }
+  return PA_OK;
+}
+
+struct DecodeCall {
+  pa::DecodeArgs args;
+  int32_t kernel;  // resolved: PA_KERNEL_VALU or PA_KERNEL_MFMA
+  Workspace ws;
+};
+
+pa_status prepare_decode(const void* q, int32_t q_dtype, int32_t num_seqs, int32_t num_q_heads,
+                         const void* k_cache, const void* v_cache, const pa_kv_cache* cache,
+                         const int32_t* block_tables, int32_t max_blocks_per_seq,
+                         const int32_t* context_lens, int32_t max_context_len, float scale, void* out,
+                         void* workspace, size_t workspace_bytes, int32_t partition_tokens, int32_t kernel,
+                         DecodeCall* call) {
+  if (!q || !k_cache || !v_cache || !cache || !block_tables || !context_lens || !out) return PA_ERR_NULL;
+  if (const pa_status s = check_cache(cache); s != PA_OK) return s;
+  if (num_seqs < 0 || num_q_heads < 1 || max_blocks_per_seq < 1 || max_context_len < 0) return PA_ERR_SHAPE;
+  if (num_q_heads % cache->num_kv_heads != 0) return PA_ERR_SHAPE;
+  if ((int64_t)max_context_len > (int64_t)max_blocks_per_seq * cache->block_size) return PA_ERR_SHAPE;
+  if (!std::isfinite(scale)) return PA_ERR_SHAPE;
+  if (num_seqs > 65535) return PA_ERR_UNSUPPORTED;
+  const bool f32_pair = q_dtype == PA_F32 && cache->dtype == PA_F32;
+  const bool bf16_q = q_dtype == PA_BF16 && (cache->dtype == PA_BF16 || cache->dtype == PA_FP8_E4M3);
+  if (!f32_pair && !bf16_q) return PA_ERR_DTYPE;
+  const int32_t group = num_q_heads / cache->num_kv_heads;
+  const int32_t P = partition_tokens == 0 ? kDefaultPartition : partition_tokens;
+  if (!valid_partition(P)) return PA_ERR_UNSUPPORTED;
+  if (kernel != PA_KERNEL_AUTO && kernel != PA_KERNEL_VALU && kernel != PA_KERNEL_MFMA) return PA_ERR_UNSUPPORTED;
+  int32_t k = kernel;
+  if (k == PA_KERNEL_AUTO) k = f32_pair ? PA_KERNEL_VALU : PA_KERNEL_MFMA;
+  if (k == PA_KERNEL_MFMA && (f32_pair || group > 16)) return PA_ERR_UNSUPPORTED;
+  if (k == PA_KERNEL_VALU && group > 8) return PA_ERR_UNSUPPORTED;
+  Workspace ws;
+  if (!workspace_layout(num_seqs, num_q_heads, cache->head_dim, max_context_len, P, &ws)) return PA_ERR_SHAPE;
+  if (ws.bytes > 0 && (!workspace || workspace_bytes < ws.bytes)) return PA_ERR_WORKSPACE;
+
+  pa::DecodeArgs& a = call->args;
+  const int32_t esz = elem_bytes(cache->dtype);
+  a.q = q;
+  a.k_cache = static_cast<const uint8_t*>(k_cache);
+  a.v_cache = static_cast<const uint8_t*>(v_cache);
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  uint8_t* wsb = static_cast<uint8_t*>(workspace);
+  a.ws_m = ws.bytes ? reinterpret_cast<float*>(wsb + ws.m_off) : nullptr;
+  a.ws_l = ws.bytes ? reinterpret_cast<float*>(wsb + ws.l_off) : nullptr;
+  a.ws_o = ws.bytes ? reinterpret_cast<float*>(wsb + ws.o_off) : nullptr;
+  a.out = out;
+  a.row_bytes = (int64_t)cache->num_kv_heads * cache->head_dim * esz;
+  a.block_bytes = a.row_bytes * cache->block_size;
+  a.num_seqs = num_seqs;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = cache->num_kv_heads;
+  a.group = group;
+  a.head_dim = cache->head_dim;
+  a.block_size = cache->block_size;
+  a.log2_bs = log2i(cache->block_size);
+  a.bt_stride = max_blocks_per_seq;
+  a.max_parts = ws.parts;
+  a.partition_tokens = P;
+  a.heads_per_wg = cache->num_kv_heads % 4 == 0 ? 4 : cache->num_kv_heads % 2 == 0 ? 2 : 1;
+  a.head_groups = cache->num_kv_heads / a.heads_per_wg;
+  a.q_fmt = q_dtype;
+  a.kv_fmt = cache->dtype;
+  const float ks = cache->dtype == PA_FP8_E4M3 ? cache->k_scale : 1.0f;
+  a.qk_scale = scale * kLog2e * ks;
+  a.v_scale = cache->dtype == PA_FP8_E4M3 ? cache->v_scale : 1.0f;
+  call->kernel = k;
+  call->ws = ws;
+  return PA_OK;
+}
+
+pa_status run_partition(const DecodeCall& c, void* stream) {
+  if (c.args.num_seqs == 0) return PA_OK;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const hipError_t e = c.kernel == PA_KERNEL_MFMA ? pa::launch_decode_mfma(c.args, s)
+                                                  : pa::launch_decode_valu(c.args, s);
+  return e == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+pa_status run_merge(const DecodeCall& c, void* stream) {
+  if (c.args.num_seqs == 0 || c.ws.parts <= 1) return PA_OK;
+  pa::MergeArgs m;
+  m.ws_m = c.args.ws_m;
+  m.ws_l = c.args.ws_l;
+  m.ws_o = c.args.ws_o;
+  m.context_lens = c.args.context_lens;
+  m.out = c.args.out;
+  m.num_seqs = c.args.num_seqs;
+  m.num_q_heads = c.args.num_q_heads;
+  m.head_dim = c.args.head_dim;
+  m.max_parts = c.ws.parts;
+  m.partition_tokens = c.args.partition_tokens;
+  m.out_fmt = c.args.q_fmt;
+  const hipError_t e = pa::launch_merge(m, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t pa_default_partition_tokens(void) { return kDefaultPartition; }
+
+size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim, int32_t max_context_len,
+                                 int32_t partition_tokens) {
+  Workspace ws;
+  const int32_t P = partition_tokens == 0 ? kDefaultPartition : partition_tokens;
+  if (!workspace_layout(num_seqs, num_q_heads, head_dim, max_context_len, P, &ws)) return 0;
+  return ws.bytes;
+}
+
+pa_status pa_write_kv(const void* k, const void* v, int32_t in_dtype, int32_t num_tokens,
+                      const int32_t* slot_mapping, void* k_cache, void* v_cache, const pa_kv_cache* cache,
+                      void* stream) {
+  if (!k || !v || !slot_mapping || !k_cache || !v_cache || !cache) return PA_ERR_NULL;
+  if (const pa_status s = check_cache(cache); s != PA_OK) return s;
+  if (num_tokens < 0) return PA_ERR_SHAPE;
+  if (cache->num_blocks * (int64_t)cache->block_size > INT32_MAX) return PA_ERR_SHAPE;
+  int32_t mode;
+  if (cache->dtype == PA_BF16 && in_dtype == PA_BF16) mode = 0;
+  else if (cache->dtype == PA_F32 && in_dtype == PA_F32) mode = 1;
+  else if (cache->dtype == PA_FP8_E4M3 && in_dtype == PA_BF16) mode = 2;
+  else if (cache->dtype == PA_FP8_E4M3 && in_dtype == PA_F32) mode = 3;
+  else return PA_ERR_DTYPE;
+  if (num_tokens == 0) return PA_OK;
+  pa::WriteArgs a;
+  a.k = k;
+  a.v = v;
+  a.slots = slot_mapping;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.num_tokens = num_tokens;
+  a.row_elems = cache->num_kv_heads * cache->head_dim;
+  a.mode = mode;
+  a.inv_k = cache->dtype == PA_FP8_E4M3 ? 1.0f / cache->k_scale : 1.0f;
+  a.inv_v = cache->dtype == PA_FP8_E4M3 ? 1.0f / cache->v_scale : 1.0f;
+  return pa::launch_write_kv(a, static_cast<hipStream_t>(stream)) == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+pa_status pa_decode_partition(const void* q, int32_t q_dtype, int32_t num_seqs, int32_t num_q_heads,
+                              const void* k_cache, const void* v_cache, const pa_kv_cache* cache,
+                              const int32_t* block_tables, int32_t max_blocks_per_seq,
+                              const int32_t* context_lens, int32_t max_context_len, float scale, void* out,
+                              void* workspace, size_t workspace_bytes, int32_t partition_tokens, int32_t kernel,
+                              void* stream) {
+  DecodeCall c;
+  const pa_status s = prepare_decode(q, q_dtype, num_seqs, num_q_heads, k_cache, v_cache, cache, block_tables,
+                                     max_blocks_per_seq, context_lens, max_context_len, scale, out, workspace,
+                                     workspace_bytes, partition_tokens, kernel, &c);
+  if (s != PA_OK) return s;
+  return run_partition(c, stream);
+}
+
+pa_status pa_decode(const void* q, int32_t q_dtype, int32_t num_seqs, int32_t num_q_heads, const void* k_cache,
+                    const void* v_cache, const pa_kv_cache* cache, const int32_t* block_tables,
+                    int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t max_context_len, float scale,
+                    void* out, void* workspace, size_t workspace_bytes, int32_t partition_tokens, int32_t kernel,
+                    void* stream) {
+  DecodeCall c;
+  pa_status s = prepare_decode(q, q_dtype, num_seqs, num_q_heads, k_cache, v_cache, cache, block_tables,
+                               max_blocks_per_seq, context_lens, max_context_len, scale, out, workspace,
+                               workspace_bytes, partition_tokens, kernel, &c);
+  if (s != PA_OK) return s;
+  s = run_partition(c, stream);
+  if (s != PA_OK) return s;
+  return run_merge(c, stream);
+}
+
+pa_status pa_merge(const void* workspace, size_t workspace_bytes, int32_t num_seqs, int32_t num_q_heads,
+                   int32_t head_dim, const int32_t* context_lens, int32_t max_context_len, int32_t partition_tokens,
+                   int32_t out_dtype, void* out, void* stream) {
+  if (!context_lens || !out) return PA_ERR_NULL;
+  if (num_seqs < 0 || num_q_heads < 1 || max_context_len < 0) return PA_ERR_SHAPE;
+  if (num_seqs > 65535) return PA_ERR_UNSUPPORTED;
+  if (out_dtype != PA_F32 && out_dtype != PA_BF16) return PA_ERR_DTYPE;
+  if (head_dim != 64 && head_dim != 128) return PA_ERR_UNSUPPORTED;
+  const int32_t P = partition_tokens == 0 ? kDefaultPartition : partition_tokens;
+  if (!valid_partition(P)) return PA_ERR_UNSUPPORTED;
+  Workspace ws;
+  if (!workspace_layout(num_seqs, num_q_heads, head_dim, max_context_len, P, &ws)) return PA_ERR_SHAPE;
+  if (ws.bytes > 0 && (!workspace || workspace_bytes < ws.bytes)) return PA_ERR_WORKSPACE;
+  if (num_seqs == 0 || ws.parts <= 1) return PA_OK;
+  const uint8_t* wsb = static_cast<const uint8_t*>(workspace);
+  pa::MergeArgs m;
+  m.ws_m = reinterpret_cast<const float*>(wsb + ws.m_off);
+  m.ws_l = reinterpret_cast<const float*>(wsb + ws.l_off);
+  m.ws_o = reinterpret_cast<const float*>(wsb + ws.o_off);
+  m.context_lens = context_lens;
+  m.out = out;
+  m.num_seqs = num_seqs;
+  m.num_q_heads = num_q_heads;
+  m.head_dim = head_dim;
+  m.max_parts = ws.parts;
+  m.partition_tokens = P;
+  m.out_fmt = out_dtype;
+  return pa::launch_merge(m, static_cast<hipStream_t>(stream)) == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+const char* pa_status_str(pa_status s) {
+  switch (s) {
+    case PA_OK: return "PA_OK";
+    case PA_ERR_NULL: return "PA_ERR_NULL: a required pointer is NULL";
+    case PA_ERR_SHAPE: return "PA_ERR_SHAPE: inconsistent or out-of-range sizes";
+    case PA_ERR_DTYPE: return "PA_ERR_DTYPE: unsupported dtype combination";
+    case PA_ERR_UNSUPPORTED: return "PA_ERR_UNSUPPORTED: unsupported head_dim, block_size, partition or kernel";
+    case PA_ERR_WORKSPACE: return "PA_ERR_WORKSPACE: workspace missing or too small";
+    case PA_ERR_HIP: return "PA_ERR_HIP: kernel launch failed";
+  }
+  return "unknown pa_status";
+}
+
+}  // extern "C"

@@ -1,0 +1,105 @@
+// Device helpers shared by the paged-KV kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+constexpr float kLog2e = 1.4426950408889634f;
+
+// -- raw loads / stores ------------------------------------------------------
+__device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+__device__ __forceinline__ u32x2 ld8(const void* p) { return *reinterpret_cast<const u32x2*>(p); }
+__device__ __forceinline__ uint32_t ld4(const void* p) { return *reinterpret_cast<const uint32_t*>(p); }
+__device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
+__device__ __forceinline__ void st8(void* p, u32x2 v) { *reinterpret_cast<u32x2*>(p) = v; }
+
+// -- bf16 -------------------------------------------------------------------
+// A bf16 value is the upper half of a float32.
+__device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Round to nearest even, two floats to one packed bf16 pair (lo in bits 0..15).
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  __bf16 a = (__bf16)lo, b = (__bf16)hi;
+  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+}
+
+// Byte permute: result = (hi.half(sel) << 16) | lo.half(sel) for 16-bit halves.
+__device__ __forceinline__ uint32_t pack_lo_halves(uint32_t lo, uint32_t hi) {
+  return __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+}
+__device__ __forceinline__ uint32_t pack_hi_halves(uint32_t lo, uint32_t hi) {
+  return __builtin_amdgcn_perm(hi, lo, 0x07060302u);
+}
+
+// -- OCP E4M3FN -------------------------------------------------------------
+// gfx950's packed fp8 -> f32 convert (OCP E4M3FN): bytes 0,1 (word 0) or 2,3 (word 1).
+__device__ __forceinline__ f32x2 e4m3x2_lo(uint32_t w) { return __builtin_amdgcn_cvt_pk_f32_fp8(w, false); }
+__device__ __forceinline__ f32x2 e4m3x2_hi(uint32_t w) { return __builtin_amdgcn_cvt_pk_f32_fp8(w, true); }
+
+// Every E4M3 value is exact in bf16, so the bf16 pattern is the upper half of the f32.
+__device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(f32x2 v) {
+  return pack_hi_halves(__float_as_uint(v.x), __float_as_uint(v.y));
+}
+
+// Round a float to E4M3FN: nearest, ties to even, saturating to +-448; NaN keeps its sign.
+__device__ __forceinline__ uint32_t f32_to_e4m3(float y) {
+  const uint32_t u = __float_as_uint(y);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const uint32_t a = u & 0x7fffffffu;
+  if (a > 0x7f800000u) return sign | 0x7fu;          // NaN
+  if (a >= 0x43e00000u) return sign | 0x7eu;         // >= 448 (and infinity): saturate
+  if (a < 0x3c800000u) {                             // below 2^-6: spacing 2^-9
+    const float t = __uint_as_float(a) * 512.0f;     // exact: scaling by a power of two
+    return sign | (uint32_t)__builtin_rintf(t);      // 0..8; 8 is the smallest normal
+  }
+  // keep 3 mantissa bits of the float, round to nearest even on bit 20
+  const uint32_t r = (a + 0x7ffffu + ((a >> 20) & 1u)) >> 20;
+  uint32_t code = r - (120u << 3);                   // float exponent bias 127 -> 7
+  code = code > 0x7eu ? 0x7eu : code;
+  return sign | code;
+}
+
+// -- wave reductions ---------------------------------------------------------
+// DPP controls: quad_perm [1,0,3,2] (xor 1), quad_perm [2,3,0,1] (xor 2),
+// row_half_mirror (lane i <-> 7-i in each 8), row_mirror (i <-> 15-i in each 16).
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xf, 0xf, false));
+}
+
+// Sum over aligned groups of N lanes (N in 1,2,4,...,64); every lane gets its group's sum.
+template <int N>
+__device__ __forceinline__ float group_sum(float x) {
+  if constexpr (N >= 2) x += dpp<0xB1>(x);
+  if constexpr (N >= 4) x += dpp<0x4E>(x);
+  if constexpr (N >= 8) x += dpp<0x141>(x);
+  if constexpr (N >= 16) x += dpp<0x140>(x);
+  if constexpr (N >= 32) x += __shfl_xor(x, 16);
+  if constexpr (N >= 64) x += __shfl_xor(x, 32);
+  return x;
+}
+
+__device__ __forceinline__ float wave_max(float x) {
+  x = fmaxf(x, dpp<0xB1>(x));
+  x = fmaxf(x, dpp<0x4E>(x));
+  x = fmaxf(x, dpp<0x141>(x));
+  x = fmaxf(x, dpp<0x140>(x));
+  x = fmaxf(x, __shfl_xor(x, 16));
+  x = fmaxf(x, __shfl_xor(x, 32));
+  return x;
+}
+
+__device__ __forceinline__ float wave_sum(float x) { return group_sum<64>(x); }
+
+}  // namespace pa

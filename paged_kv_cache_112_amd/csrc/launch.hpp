@@ -1,0 +1,58 @@
+// Host-side launch descriptors passed from the C ABI layer to each kernel file.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+struct WriteArgs {
+  const void* k;
+  const void* v;
+  const int32_t* slots;
+  void* k_cache;
+  void* v_cache;
+  int32_t num_tokens;
+  int32_t row_elems;   // H_kv * head_dim
+  int32_t mode;        // 0 bf16 copy, 1 f32 copy, 2 bf16 -> e4m3, 3 f32 -> e4m3
+  float inv_k, inv_v;  // fp32(1 / scale) for e4m3 pools
+};
+
+// Storage formats, numbered as pa_dtype in include/pa.h.
+enum Fmt : int32_t { kF32 = 0, kBf16 = 1, kE4m3 = 2 };
+
+struct DecodeArgs {
+  const void* q;             // [B, H_q, D]
+  const uint8_t* k_cache;    // [num_blocks, bs, H_kv, D]
+  const uint8_t* v_cache;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  float* ws_m;               // [B, H_q, max_parts]
+  float* ws_l;               // [B, H_q, max_parts]
+  float* ws_o;               // [B, H_q, max_parts, D]
+  void* out;                 // [B, H_q, D], q's format
+  int64_t row_bytes;         // H_kv * D * elem
+  int64_t block_bytes;       // bs * row_bytes
+  int32_t num_seqs, num_q_heads, num_kv_heads, group, head_dim;
+  int32_t block_size, log2_bs, bt_stride, max_parts, partition_tokens;
+  int32_t heads_per_wg, head_groups;
+  int32_t q_fmt, kv_fmt;
+  float qk_scale;            // scale * log2(e) * k_scale
+  float v_scale;
+};
+
+struct MergeArgs {
+  const float* ws_m;
+  const float* ws_l;
+  const float* ws_o;
+  const int32_t* context_lens;
+  void* out;
+  int32_t num_seqs, num_q_heads, head_dim, max_parts, partition_tokens, out_fmt;
+};
+
+hipError_t launch_write_kv(const WriteArgs& a, hipStream_t stream);
+hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_decode_valu(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_merge(const MergeArgs& a, hipStream_t stream);
+
+}  // namespace pa

@@ -1,0 +1,93 @@
+// pa_write_kv kernels: scatter new tokens' K and V rows into the block pools.
+//
+// The pool [num_blocks, block_size, H_kv, d_h] seen as [num_blocks * block_size,
+// H_kv * d_h] is slot-major, so token i's whole row (all KV heads) is one
+// contiguous run of bytes at slot_mapping[i] (LLM stack book 4.6, "From Python
+// bookkeeping to the tensors the kernel actually takes": the write is one
+// indexed copy over the flattened pool).  Each thread moves one 8-element
+// chunk of a row for K and the same chunk for V: loads and stores of
+// neighbouring threads are contiguous, 16 bytes wide for bf16.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace pa {
+
+enum class WriteMode { kCopy16, kCopy32, kBf16ToE4m3, kF32ToE4m3 };
+
+template <WriteMode M>
+__global__ __launch_bounds__(256) void write_kv_kernel(const uint8_t* __restrict__ k, const uint8_t* __restrict__ v,
+                                                       const int32_t* __restrict__ slots, uint8_t* __restrict__ kc,
+                                                       uint8_t* __restrict__ vc, int64_t total_chunks,
+                                                       int32_t chunks_per_row, float inv_k, float inv_v) {
+  const int64_t item = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (item >= total_chunks) return;
+  const int64_t tok = item / chunks_per_row;
+  const int32_t c = (int32_t)(item - tok * chunks_per_row);
+  const int32_t slot = slots[tok];
+  if (slot < 0) return;
+  const int64_t src_elem = item * 8;                                   // == tok * row + c * 8
+  const int64_t dst_elem = (int64_t)slot * chunks_per_row * 8 + (int64_t)c * 8;
+  if constexpr (M == WriteMode::kCopy16) {                             // bf16 -> bf16
+    st16(kc + dst_elem * 2, ld16(k + src_elem * 2));
+    st16(vc + dst_elem * 2, ld16(v + src_elem * 2));
+  } else if constexpr (M == WriteMode::kCopy32) {                      // f32 -> f32
+    const u32x4 k0 = ld16(k + src_elem * 4), k1 = ld16(k + src_elem * 4 + 16);
+    const u32x4 v0 = ld16(v + src_elem * 4), v1 = ld16(v + src_elem * 4 + 16);
+    st16(kc + dst_elem * 4, k0);
+    st16(kc + dst_elem * 4 + 16, k1);
+    st16(vc + dst_elem * 4, v0);
+    st16(vc + dst_elem * 4 + 16, v1);
+  } else {
+    float xk[8], xv[8];
+    if constexpr (M == WriteMode::kBf16ToE4m3) {
+      const u32x4 a = ld16(k + src_elem * 2), b = ld16(v + src_elem * 2);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        xk[2 * i] = bf16lo(a[i]); xk[2 * i + 1] = bf16hi(a[i]);
+        xv[2 * i] = bf16lo(b[i]); xv[2 * i + 1] = bf16hi(b[i]);
+      }
+    } else {
+      const u32x4 a0 = ld16(k + src_elem * 4), a1 = ld16(k + src_elem * 4 + 16);
+      const u32x4 b0 = ld16(v + src_elem * 4), b1 = ld16(v + src_elem * 4 + 16);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        xk[i] = __uint_as_float(a0[i]); xk[4 + i] = __uint_as_float(a1[i]);
+        xv[i] = __uint_as_float(b0[i]); xv[4 + i] = __uint_as_float(b1[i]);
+      }
+    }
+    u32x2 ok = {0u, 0u}, ov = {0u, 0u};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      // one fp32 multiply, then round to E4M3 (no fused multiply-add is possible here)
+      ok[i >> 2] |= f32_to_e4m3(xk[i] * inv_k) << (8 * (i & 3));
+      ov[i >> 2] |= f32_to_e4m3(xv[i] * inv_v) << (8 * (i & 3));
+    }
+    st8(kc + dst_elem, ok);
+    st8(vc + dst_elem, ov);
+  }
+}
+
+hipError_t launch_write_kv(const WriteArgs& a, hipStream_t stream) {
+  const int32_t cpr = a.row_elems / 8;
+  const int64_t total = (int64_t)a.num_tokens * cpr;
+  if (total == 0) return hipSuccess;
+  const dim3 block(256);
+  const dim3 grid((unsigned)((total + 255) / 256));
+  const uint8_t* k = static_cast<const uint8_t*>(a.k);
+  const uint8_t* v = static_cast<const uint8_t*>(a.v);
+  uint8_t* kc = static_cast<uint8_t*>(a.k_cache);
+  uint8_t* vc = static_cast<uint8_t*>(a.v_cache);
+  switch (a.mode) {
+    case 0: hipLaunchKernelGGL(write_kv_kernel<WriteMode::kCopy16>, grid, block, 0, stream, k, v, a.slots, kc, vc,
+                               total, cpr, a.inv_k, a.inv_v); break;
+    case 1: hipLaunchKernelGGL(write_kv_kernel<WriteMode::kCopy32>, grid, block, 0, stream, k, v, a.slots, kc, vc,
+                               total, cpr, a.inv_k, a.inv_v); break;
+    case 2: hipLaunchKernelGGL(write_kv_kernel<WriteMode::kBf16ToE4m3>, grid, block, 0, stream, k, v, a.slots, kc,
+                               vc, total, cpr, a.inv_k, a.inv_v); break;
+    default: hipLaunchKernelGGL(write_kv_kernel<WriteMode::kF32ToE4m3>, grid, block, 0, stream, k, v, a.slots, kc,
+                                vc, total, cpr, a.inv_k, a.inv_v); break;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace pa

@@ -1,0 +1,129 @@
+"""The C-ABI library loads, exports what include/pa.h declares, and rejects bad arguments on the host.
+
+No GPU is needed: every call here fails a host-side check and returns before
+anything is enqueued.  Fake non-null addresses are never dereferenced.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import paged_kv_cache_112_amd as pa
+from conftest import ROOT
+
+FAKE = 0x1000  # a non-null address the library must not touch (it returns before any launch)
+
+
+def _declared_functions():
+    with open(os.path.join(ROOT, "include", "pa.h")) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pa_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    lib = ctypes.CDLL(pa.LIB_PATH)
+    declared = _declared_functions()
+    assert set(declared) == set(pa.EXPORTED)
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_status_strings():
+    for s in range(7):
+        assert pa.status_str(s).startswith("PA_")
+    assert pa.pa_default_partition_tokens() == 256
+
+
+def test_workspace_bytes():
+    # one partition: no workspace
+    assert pa.pa_decode_workspace_bytes(64, 32, 128, 256, 0) == 0
+    # cfg2-sized: J = ceil(3360/256) = 14
+    rows = 64 * 32 * 14
+    al = lambda x: (x + 255) // 256 * 256
+    assert pa.pa_decode_workspace_bytes(64, 32, 128, 3360, 0) == 2 * al(rows * 4) + al(rows * 128 * 4)
+    assert pa.pa_decode_workspace_bytes(4, 4, 64, 200, 16) == 2 * al(4 * 4 * 13 * 4) + al(4 * 4 * 13 * 64 * 4)
+    assert pa.pa_decode_workspace_bytes(4, 4, 64, 200, 17) == 0        # invalid partition size
+    assert pa.pa_decode_workspace_bytes(-1, 4, 64, 200, 0) == 0
+
+
+def _cache(**kw):
+    d = dict(num_blocks=64, block_size=16, num_kv_heads=2, head_dim=64, dtype=pa.PA_F32, k_scale=1.0, v_scale=1.0)
+    d.update(kw)
+    return pa.PaKvCache(d["num_blocks"], d["block_size"], d["num_kv_heads"], d["head_dim"], d["dtype"],
+                        d["k_scale"], d["v_scale"])
+
+
+def _decode(**kw):
+    a = dict(q=FAKE, q_dtype=pa.PA_F32, num_seqs=4, num_q_heads=4, k_cache=FAKE, v_cache=FAKE, cache=_cache(),
+             block_tables=FAKE, max_blocks_per_seq=13, context_lens=FAKE, max_context_len=200, scale=0.125,
+             out=FAKE, workspace=FAKE, workspace_bytes=1 << 30, partition_tokens=0, kernel=0, stream=None)
+    a.update(kw)
+    return pa.pa_decode(**a)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), pa.PA_ERR_NULL),
+    (dict(out=None), pa.PA_ERR_NULL),
+    (dict(block_tables=None), pa.PA_ERR_NULL),
+    (dict(num_q_heads=5), pa.PA_ERR_SHAPE),                              # H_q % H_kv != 0
+    (dict(max_context_len=13 * 16 + 1), pa.PA_ERR_SHAPE),               # beyond the table
+    (dict(num_seqs=-1), pa.PA_ERR_SHAPE),
+    (dict(scale=float("nan")), pa.PA_ERR_SHAPE),
+    (dict(q_dtype=pa.PA_BF16), pa.PA_ERR_DTYPE),                        # bf16 q with an f32 pool
+    (dict(cache=_cache(head_dim=96)), pa.PA_ERR_UNSUPPORTED),
+    (dict(cache=_cache(block_size=24)), pa.PA_ERR_UNSUPPORTED),
+    (dict(cache=_cache(dtype=7)), pa.PA_ERR_DTYPE),
+    (dict(partition_tokens=100), pa.PA_ERR_UNSUPPORTED),
+    (dict(kernel=pa.PA_KERNEL_MFMA), pa.PA_ERR_UNSUPPORTED),            # f32 has no matrix-core path
+    (dict(kernel=9), pa.PA_ERR_UNSUPPORTED),
+    (dict(num_q_heads=32, cache=_cache(num_kv_heads=2), kernel=pa.PA_KERNEL_VALU), pa.PA_ERR_UNSUPPORTED),
+    (dict(workspace=None, partition_tokens=16), pa.PA_ERR_WORKSPACE),
+    (dict(workspace_bytes=100, partition_tokens=16), pa.PA_ERR_WORKSPACE),
+    (dict(cache=_cache(dtype=pa.PA_FP8_E4M3, k_scale=0.0), q_dtype=pa.PA_BF16), pa.PA_ERR_SHAPE),
+])
+def test_decode_rejects_bad_arguments(kw, status):
+    assert _decode(**kw) == status
+
+
+def test_decode_partition_and_merge_checks():
+    assert pa.pa_decode_partition(None, 0, 1, 1, FAKE, FAKE, _cache(), FAKE, 1, FAKE, 1, 1.0, FAKE, None, 0,
+                                  0, 0, None) == pa.PA_ERR_NULL
+    assert pa.pa_merge(FAKE, 1 << 20, 4, 4, 64, None, 200, 16, pa.PA_F32, FAKE, None) == pa.PA_ERR_NULL
+    assert pa.pa_merge(FAKE, 1 << 20, 4, 4, 64, FAKE, 200, 16, pa.PA_FP8_E4M3, FAKE, None) == pa.PA_ERR_DTYPE
+    assert pa.pa_merge(FAKE, 1 << 20, 4, 4, 96, FAKE, 200, 16, pa.PA_F32, FAKE, None) == pa.PA_ERR_UNSUPPORTED
+    assert pa.pa_merge(FAKE, 10, 4, 4, 64, FAKE, 200, 16, pa.PA_F32, FAKE, None) == pa.PA_ERR_WORKSPACE
+    # a single partition needs no workspace and enqueues nothing
+    assert pa.pa_merge(None, 0, 4, 4, 64, FAKE, 16, 16, pa.PA_F32, FAKE, None) == pa.PA_OK
+
+
+def test_zero_sized_calls_enqueue_nothing():
+    assert _decode(num_seqs=0) == pa.PA_OK
+    c = _cache(dtype=pa.PA_BF16)
+    assert pa.pa_write_kv(FAKE, FAKE, pa.PA_BF16, 0, FAKE, FAKE, FAKE, c, None) == pa.PA_OK
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(k=None), pa.PA_ERR_NULL),
+    (dict(slot_mapping=None), pa.PA_ERR_NULL),
+    (dict(num_tokens=-3), pa.PA_ERR_SHAPE),
+    (dict(in_dtype=pa.PA_F32), pa.PA_ERR_DTYPE),                                      # f32 into bf16 pool
+    (dict(cache=_cache(dtype=pa.PA_FP8_E4M3), in_dtype=pa.PA_FP8_E4M3), pa.PA_ERR_DTYPE),
+    (dict(cache=_cache(dtype=pa.PA_FP8_E4M3, v_scale=float("inf"))), pa.PA_ERR_SHAPE),
+    (dict(cache=_cache(dtype=pa.PA_BF16, num_blocks=1 << 28, block_size=16)), pa.PA_ERR_SHAPE),
+    (dict(cache=_cache(dtype=pa.PA_BF16, head_dim=80)), pa.PA_ERR_UNSUPPORTED),
+])
+def test_write_rejects_bad_arguments(kw, status):
+    a = dict(k=FAKE, v=FAKE, in_dtype=pa.PA_BF16, num_tokens=4, slot_mapping=FAKE, k_cache=FAKE, v_cache=FAKE,
+             cache=_cache(dtype=pa.PA_BF16), stream=None)
+    a.update(kw)
+    assert pa.pa_write_kv(**a) == status
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    from paged_kv_cache_112_amd import _binding
+    monkeypatch.setattr(_binding, "_lib", None)
+    monkeypatch.setattr(_binding, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="not built"):
+        _binding.lib()
