@@ -1,0 +1,327 @@
+"""Benchmark of the paged-KV hot path on one MI355X.
+
+Workload: one Llama-3-8B attention layer (32 query heads, 8 KV heads, head dim
+128, bf16), batch 64, block size 16, context lengths = prompt U[100,2000] +
+output U[20,1500] from the seeded generator, physical blocks shuffled over a
+pool 10 % larger than needed.  One step is the whole hot path for one batch:
+pa_write_kv of this step's 64 tokens, then pa_decode (partition kernel + merge).
+Each step uses the next of L layer-pool copies, as a model's layers would, so
+the 256 MB MALL cannot serve a pool read by an earlier step.
+
+Prints one JSON line: value = algorithmic bytes of the step / step time (GB/s);
+roofline = the partition kernel (the dominant one) against HBM peak, timed
+live with HIP events on the stream it runs on; cpu_baseline = the CPU oracle.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+WORKLOAD = "llama3_8b_b64"
+HBM_PEAK_GBS = 8000.0
+LAYERS = 8
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_partition_llama3_8b_b64.traffic.json")
+KERNEL_SOURCES = ["paged_kv_cache_112_amd/csrc/decode_mfma.hip", "paged_kv_cache_112_amd/csrc/common.hpp"]
+
+
+def algorithmic_bytes(w, kv_bytes=2, q_bytes=2, out_bytes=2, in_bytes=2):
+    """Bytes the method itself must move (no partials, no re-reads).
+
+    decode: every context token's K and V row for every KV head, the q rows
+    in, the out rows out, one int32 table entry per block read and one int32
+    context length per sequence.  write: each new row in and out, plus its slot.
+    """
+    ctx = w.context_lens.astype(np.int64)
+    kv = int(ctx.sum()) * w.num_kv_heads * w.head_dim * 2 * kv_bytes
+    q = w.num_seqs * w.num_q_heads * w.head_dim * q_bytes
+    out = w.num_seqs * w.num_q_heads * w.head_dim * out_bytes
+    tables = 4 * int(((ctx + w.block_size - 1) // w.block_size).sum()) + 4 * w.num_seqs
+    write = w.num_seqs * w.num_kv_heads * w.head_dim * 2 * (in_bytes + kv_bytes) + 4 * w.num_seqs
+    return {"partition": kv + q + tables, "decode": kv + q + out + tables, "write": write,
+            "step": kv + q + out + tables + write, "kv": kv}
+
+
+def kernel_sha() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per partition-kernel launch from the committed rocprofv3 counter runs, if still current."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_sha") != kernel_sha():
+        return None
+    return t.get("bytes_per_launch")
+
+
+def cpu_baseline(w):
+    """The oracle, as it stands, on the same decode workload (all 64 sequences), on host cores."""
+    import oracle
+    from threadpoolctl import threadpool_limits
+    from workloads import f32_to_bf16_bits
+
+    shape = (w.num_blocks, w.block_size, w.num_kv_heads, w.head_dim)
+    kc = np.full(shape, 0x7FC0, dtype=np.uint16)
+    vc = np.full(shape, 0x7FC0, dtype=np.uint16)
+    for b in range(w.num_seqs):
+        pos = w.owned_positions(b)
+        oracle.write_kv(kc, vc, f32_to_bf16_bits(w.seq_token_values("k", b)),
+                        f32_to_bf16_bits(w.seq_token_values("v", b)), w.slots(b, pos), "bf16", "bf16")
+    q = f32_to_bf16_bits(w.q_values())
+    times = []
+    with threadpool_limits(limits=1):
+        deadline = time.perf_counter() + 20.0
+        while len(times) < 3 or (time.perf_counter() < deadline and len(times) < 10):
+            t0 = time.perf_counter()
+            oracle.decode(q, kc, vc, w.block_tables, w.context_lens, w.scale, "bf16", "bf16")
+            times.append(time.perf_counter() - t0)
+            if sum(times) > 30.0:
+                break
+    t = statistics.median(times)
+    nbytes = algorithmic_bytes(w)["decode"]
+    return {"value": round(nbytes / t / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "tokens_per_s": round(w.num_seqs / t, 2), "seconds_per_decode": round(t, 4),
+            "sample": f"full {WORKLOAD} decode (64 sequences, sum ctx {w.total_tokens}), fp64 numpy, "
+                      f"one thread, median of {len(times)} runs"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--partition", type=int, default=0, help="partition tokens (0 = library default)")
+    ap.add_argument("--kernel", type=int, default=0, help="0 auto, 1 vector path, 2 matrix-core, 3 matrix-core persistent")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--workload", default=WORKLOAD,
+                    choices=["llama3_8b_b64", "llama3_8b_long", "llama2_7b_mha", "llama3_8b_fp8_prefix"])
+    ap.add_argument("--block-size", type=int, default=None, help="block size for llama2_7b_mha")
+    ap.add_argument("--copy-calibrate", type=int, default=0, metavar="MIB",
+                    help="only copy MIB MiB with torch (a plain copy of known size, for counter scaling)")
+    ap.add_argument("--contiguous", action="store_true",
+                    help="identity-ordered block tables (each sequence's blocks adjacent): the contiguous comparator")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the paged-KV path here is "
+              "single-GPU, see the design notes for how it would shard.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import paged_kv_cache_112_amd as pa
+    from workloads import f32_to_bf16_bits, make_config
+
+    if args.copy_calibrate:
+        n = args.copy_calibrate << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_read": n, "copy_calibration_bytes_written": n, "launches": 3}))
+        return
+
+    if not os.path.exists(pa.LIB_PATH):
+        from paged_kv_cache_112_amd.build import build
+        build()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = make_config(args.workload, args.block_size) if args.workload == "llama2_7b_mha" else make_config(args.workload)
+    if args.contiguous:
+        from workloads import deal_tables
+        w.block_tables, _ = deal_tables(w.context_lens, w.block_size, np.arange(w.num_blocks, dtype=np.int32))
+    B, hq, hkv, d, bs = w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim, w.block_size
+
+    def to_dev(a):
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(a).to(dev)
+
+    # ---- inputs resident in HBM: pools filled with every token but this step's ---------------
+    # Values are seeded N(0,1) drawn on the device (bf16), written through pa_write_kv.
+    fp8 = w.kv_dtype == "e4m3"
+    kv_dtype = torch.uint8 if fp8 else torch.bfloat16
+    k_scale, v_scale = (float(np.float32(4.8 / 448)), float(np.float32(4.8 / 448))) if fp8 else (1.0, 1.0)
+    shape = (w.num_blocks, bs, hkv, d)
+    k0 = torch.zeros(shape, dtype=kv_dtype, device=dev)
+    v0 = torch.zeros(shape, dtype=kv_dtype, device=dev)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(w.seed)
+    for b in range(B):
+        pos = w.owned_positions(b)[:-1]
+        if len(pos) == 0:
+            continue
+        K = torch.randn((len(pos), hkv, d), generator=gen, device=dev).to(torch.bfloat16)
+        V = torch.randn((len(pos), hkv, d), generator=gen, device=dev).to(torch.bfloat16)
+        pa.write_kv(K, V, to_dev(w.slots(b, pos).astype(np.int32)), k0, v0, k_scale, v_scale)
+    k_new = torch.randn((B, hkv, d), generator=gen, device=dev).to(torch.bfloat16)
+    v_new = torch.randn((B, hkv, d), generator=gen, device=dev).to(torch.bfloat16)
+    slots = to_dev(w.append_slots())
+    q = torch.randn((B, hq, d), generator=gen, device=dev).to(torch.bfloat16)
+    bt = to_dev(w.block_tables)
+    ctx = to_dev(w.context_lens)
+    max_ctx = int(w.context_lens.max())
+    pools = [(k0, v0)] + [(k0.clone(), v0.clone()) for _ in range(LAYERS - 1)]
+    out = torch.empty((B, hq, d), dtype=torch.bfloat16, device=dev)
+    P = args.partition or pa.pa_default_partition_tokens()
+    ws = pa.new_workspace(B, hq, d, max_ctx, P, dev)
+    if ws is None:
+        ws = torch.empty(1, dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+
+    def step(i, ev=None):
+        kc, vc = pools[i % LAYERS]
+        if ev is not None:
+            ev[0].record(stream)
+        pa.write_kv(k_new, v_new, slots, kc, vc, k_scale, v_scale)
+        if ev is not None:
+            ev[1].record(stream)
+        pa.decode_partition(q, kc, vc, bt, ctx, w.scale, out=out, max_context_len=max_ctx, workspace=ws,
+                            partition_tokens=P, kernel=args.kernel, k_scale=k_scale, v_scale=v_scale)
+        if ev is not None:
+            ev[2].record(stream)
+        pa.merge(ws, ctx, out, max_ctx, P)
+        if ev is not None:
+            ev[3].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    eager_out = out.clone()                      # result of step warmup-1 (every layer holds the same data)
+
+    # ---- HIP graphs: one per layer's step, and one of all LAYERS steps in order (as a model's
+    # forward pass would replay them); replays cost no per-kernel host work --------------------
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    graphs = []
+    with torch.cuda.stream(side):
+        for i in range(LAYERS):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=side):
+                step(i)
+            graphs.append(g)
+        all_layers = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(all_layers, stream=side):
+            for i in range(LAYERS):
+                step(i)
+    stream.wait_stream(side)
+    torch.cuda.synchronize()
+    for i, g in enumerate(graphs + [all_layers]):   # every replay must reproduce the eager result exactly
+        out.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        if not torch.equal(out.view(torch.int16), eager_out.view(torch.int16)):
+            raise SystemExit(f"graph replay {i} differs from the eager step")
+
+    # ---- timed region: exactly K steps ----------------------------------------------------------
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for _ in range(args.steps // LAYERS):
+        all_layers.replay()
+    for i in range(args.steps % LAYERS):
+        graphs[i].replay()
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = t_start.elapsed_time(t_end) / args.steps
+
+    # ---- the dominant kernel alone: back-to-back launches between two events --------------------
+    part_graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(part_graph, stream=side):
+            for i in range(LAYERS):
+                kc, vc = pools[i]
+                pa.decode_partition(q, kc, vc, bt, ctx, w.scale, out=out, max_context_len=max_ctx,
+                                    workspace=ws, partition_tokens=P, kernel=args.kernel, k_scale=k_scale,
+                                    v_scale=v_scale)
+    stream.wait_stream(side)
+    torch.cuda.synchronize()
+    reps = max(1, args.steps // LAYERS)
+    p_start = torch.cuda.Event(enable_timing=True)
+    p_end = torch.cuda.Event(enable_timing=True)
+    p_start.record(stream)
+    for _ in range(reps):
+        part_graph.replay()
+    p_end.record(stream)
+    torch.cuda.synchronize()
+    part_launch_ms = p_start.elapsed_time(p_end) / (reps * LAYERS)
+
+    # ---- per-kernel durations: HIP events on the library's stream, queue kept full ------------
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    try:
+        torch.cuda._sleep(200_000_000)           # GPU busy while the host enqueues every step
+    except (AttributeError, RuntimeError):
+        pass
+    for i in range(args.steps):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    write_ms = statistics.mean(e[0].elapsed_time(e[1]) for e in evs)
+    part_ms = statistics.mean(e[1].elapsed_time(e[2]) for e in evs)
+    merge_ms = statistics.mean(e[2].elapsed_time(e[3]) for e in evs)
+    eager_ms = (evs[0][0].elapsed_time(evs[-1][3])) / max(1, args.steps - 1) if args.steps > 1 else None
+
+    nb = algorithmic_bytes(w, kv_bytes=1 if fp8 else 2)
+    value = nb["step"] / (ms_per_step * 1e-3) / 1e9
+    achieved = nb["partition"] / (part_launch_ms * 1e-3) / 1e9
+    traffic = measured_traffic()
+    result = {
+        "metric": "paged-attn decode achieved HBM GB/s + tokens/s, Llama-3-8B layer, batch 64",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "tokens_per_s": round(B / (ms_per_step * 1e-3), 1),
+        "kv_tokens_per_s": round(w.total_tokens / (ms_per_step * 1e-3), 1),
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16 q / e4m3 kv" if fp8 else "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": B, "num_q_heads": hq, "num_kv_heads": hkv, "head_dim": d,
+                   "block_size": bs, "sum_context": w.total_tokens, "max_context": max_ctx,
+                   "partition_tokens": P, "kernel": ["auto", "valu", "mfma", "mfma_persist"][args.kernel],
+                   "layer_pools_rotated": LAYERS, "step": "pa_write_kv(64 tokens) + pa_decode",
+                   "block_order": "identity (contiguous comparator)" if args.contiguous else "seeded permutation"},
+        "kernel_us": {"write_kv": round(write_ms * 1e3, 2), "decode_partition": round(part_ms * 1e3, 2),
+                      "merge": round(merge_ms * 1e3, 2)},
+        "decode_partition_us_back_to_back": round(part_launch_ms * 1e3, 2),
+        "timing": "steps replayed from a HIP graph of the 8 layer steps; kernel_us: HIP events around each "
+                  "eager launch queued behind a busy GPU (each pair adds a few us); roofline: HIP events "
+                  "around back-to-back replays of the partition kernel alone",
+        "eager_ms_per_step": round(eager_ms, 5) if eager_ms else None,
+        "bytes": nb,
+        "roofline": {"bound": "hbm", "kernel": "decode_mfma_kernel (partition stage)",
+                     "bytes_per_launch": nb["partition"],
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic},
+    }
+    if not args.no_cpu_baseline and args.workload == WORKLOAD:
+        result["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(result))
+
+
+if __name__ == "__main__":
+    main()

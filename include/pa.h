@@ -106,19 +106,24 @@ pa_status pa_write_kv(const void* k, const void* v, int32_t in_dtype, int32_t nu
 int32_t pa_default_partition_tokens(void);
 
 /* Workspace bytes pa_decode / pa_decode_partition / pa_merge need for this shape
- * (0 when max_context_len fits in one partition).  partition_tokens = 0 means
- * the default.  Layout, each region aligned to 256 bytes:
+ * (0 when max_context_len fits in one partition).  partition_tokens = 0 means the
+ * default.  Layout, each region aligned to 256 bytes:
  *   m [num_seqs, num_q_heads, J] f32, l [num_seqs, num_q_heads, J] f32,
  *   o [num_seqs, num_q_heads, J, head_dim] f32,  J = ceil(max_context_len / P).
+ * Calls that share a workspace must be ordered on one stream (they race otherwise).
  * Returns 0 for invalid arguments. */
 size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
                                  int32_t max_context_len, int32_t partition_tokens);
 
 /* Kernel selection for pa_decode / pa_decode_partition. */
 typedef enum pa_kernel {
-  PA_KERNEL_AUTO = 0,     /* matrix-core path for bf16/e4m3 pools, vector path for f32 */
-  PA_KERNEL_VALU = 1,     /* vector-ALU path (all formats, query-head group <= 8) */
-  PA_KERNEL_MFMA = 2      /* matrix-core path (bf16 q with bf16 or e4m3 pools, group <= 16) */
+  PA_KERNEL_AUTO = 0,      /* matrix-core path for bf16/e4m3 pools, vector path for f32 */
+  PA_KERNEL_VALU = 1,      /* vector-ALU path (all formats, query-head group <= 8) */
+  PA_KERNEL_MFMA = 2,      /* matrix-core path, one workgroup per (sequence, partition, up to
+                              four KV heads) (bf16 q with bf16 or e4m3 pools, group <= 16) */
+  PA_KERNEL_MFMA_PERSIST = 3 /* matrix-core path, persistent workgroups that each stream a
+                              contiguous range of work units (same inputs; num_seqs > 1024
+                              runs PA_KERNEL_MFMA instead) */
 } pa_kernel;
 
 /* Paged decode attention for one new token per sequence.

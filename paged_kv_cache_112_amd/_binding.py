@@ -18,7 +18,7 @@ PA_OK, PA_ERR_NULL, PA_ERR_SHAPE, PA_ERR_DTYPE, PA_ERR_UNSUPPORTED, PA_ERR_WORKS
 # pa_dtype
 PA_F32, PA_BF16, PA_FP8_E4M3 = 0, 1, 2
 # pa_kernel
-PA_KERNEL_AUTO, PA_KERNEL_VALU, PA_KERNEL_MFMA = 0, 1, 2
+PA_KERNEL_AUTO, PA_KERNEL_VALU, PA_KERNEL_MFMA, PA_KERNEL_MFMA_PERSIST = 0, 1, 2, 3
 
 EXPORTED = ("pa_write_kv", "pa_decode", "pa_decode_partition", "pa_merge", "pa_decode_workspace_bytes",
             "pa_default_partition_tokens", "pa_status_str")
@@ -170,6 +170,14 @@ def decode_workspace_bytes(num_seqs, num_q_heads, head_dim, max_context_len, par
     return pa_decode_workspace_bytes(num_seqs, num_q_heads, head_dim, max_context_len, partition_tokens)
 
 
+def new_workspace(num_seqs, num_q_heads, head_dim, max_context_len, partition_tokens=0, device="cuda"):
+    """A workspace of the required size, or None when the shape needs none."""
+    need = pa_decode_workspace_bytes(num_seqs, num_q_heads, head_dim, max_context_len, partition_tokens)
+    if need == 0:
+        return None
+    return _torch().empty(need, dtype=_torch().uint8, device=device)
+
+
 def _decode_common(fn, q, k_cache, v_cache, block_tables, context_lens, scale, out, max_context_len, workspace,
                    partition_tokens, kernel, k_scale, v_scale, stream):
     torch = _torch()
@@ -185,9 +193,8 @@ def _decode_common(fn, q, k_cache, v_cache, block_tables, context_lens, scale, o
         max_context_len = block_tables.shape[1] * bs
     if out is None:
         out = torch.empty_like(q)
-    need = pa_decode_workspace_bytes(B, hq, d, max_context_len, partition_tokens)
-    if workspace is None and need:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if workspace is None:
+        workspace = new_workspace(B, hq, d, max_context_len, partition_tokens, q.device)
     ws_ptr = _ptr(workspace) if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     desc = cache_desc(k_cache, k_scale, v_scale)

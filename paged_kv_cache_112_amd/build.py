@@ -17,13 +17,17 @@ LIB_NAME = "libpa.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
 ARCH = "gfx950"
 
-SOURCES = ["api.cpp", "write_kv.hip", "decode_mfma.hip", "decode_valu.hip", "merge.hip"]
+SOURCES = ["api.cpp", "write_kv.hip", "decode_mfma.hip", "decode_persist.hip", "decode_valu.hip", "merge.hip"]
 
-# Packed-fp32 instructions are disabled on purpose; fp32 denormals are kept.
+# Packed-fp32 instructions are disabled on purpose; fp32 denormals are kept.  The
+# atomic optimizer is off: it turns the one-lane work-counter atomic of the persistent
+# decode kernel into a wave-aggregated one whose result is read at once, which makes
+# the wave wait for every load it has in flight.
 COMMON_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-fno-gpu-flush-denormals-to-zero",
+    "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
     "-Wall", "-Wno-unused-function", "-Wno-unused-command-line-argument",
     "-I" + os.path.join(ROOT, "include"),
 ]
@@ -44,10 +48,11 @@ def _compile(args):
     return r.stderr
 
 
-def build(verbose: bool = False, extra_flags: list[str] | None = None) -> str:
-    """Compile every source for gfx950 and link ``libpa.so``; returns its path."""
+def build(verbose: bool = False, extra_flags: list[str] | None = None, out_path: str | None = None) -> str:
+    """Compile every source for gfx950 and link ``libpa.so`` (or ``out_path``); returns its path."""
     cc = hipcc()
-    obj_dir = os.path.join(HERE, "_build")
+    lib_path = out_path or LIB_PATH
+    obj_dir = os.path.join(HERE, "_build") if out_path is None else lib_path + ".objs"
     os.makedirs(obj_dir, exist_ok=True)
     flags = COMMON_FLAGS + list(extra_flags or [])
     jobs, objs = [], []
@@ -60,13 +65,13 @@ def build(verbose: bool = False, extra_flags: list[str] | None = None) -> str:
         for log in ex.map(_compile, jobs):
             if verbose and log.strip():
                 print(log)
-    tmp = LIB_PATH + ".tmp"
+    tmp = lib_path + ".tmp"
     link = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(link, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB_PATH)
-    return LIB_PATH
+    os.replace(tmp, lib_path)
+    return lib_path
 
 
 if __name__ == "__main__":

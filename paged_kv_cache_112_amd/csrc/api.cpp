@@ -6,6 +6,7 @@
 #include <cstdint>
 
 #include "../../include/pa.h"
+#include "common.hpp"
 #include "launch.hpp"
 
 namespace {
@@ -13,6 +14,9 @@ namespace {
 constexpr int32_t kDefaultPartition = 256;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr size_t kAlign = 256;
+#ifndef PA_MAX_HEADS_PER_WG
+#define PA_MAX_HEADS_PER_WG 4
+#endif
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
@@ -46,7 +50,7 @@ bool workspace_layout(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim, i
   }
   const size_t rows = (size_t)num_seqs * (size_t)num_q_heads * (size_t)parts;
   w->m_off = 0;
-  w->l_off = align_up(rows * 4);
+  w->l_off = w->m_off + align_up(rows * 4);
   w->o_off = w->l_off + align_up(rows * 4);
   w->bytes = w->o_off + align_up(rows * (size_t)head_dim * 4);
   return true;
@@ -90,10 +94,11 @@ pa_status prepare_decode(const void* q, int32_t q_dtype, int32_t num_seqs, int32
   const int32_t group = num_q_heads / cache->num_kv_heads;
   const int32_t P = partition_tokens == 0 ? kDefaultPartition : partition_tokens;
   if (!valid_partition(P)) return PA_ERR_UNSUPPORTED;
-  if (kernel != PA_KERNEL_AUTO && kernel != PA_KERNEL_VALU && kernel != PA_KERNEL_MFMA) return PA_ERR_UNSUPPORTED;
+  if (kernel < PA_KERNEL_AUTO || kernel > PA_KERNEL_MFMA_PERSIST) return PA_ERR_UNSUPPORTED;
   int32_t k = kernel;
   if (k == PA_KERNEL_AUTO) k = f32_pair ? PA_KERNEL_VALU : PA_KERNEL_MFMA;
-  if (k == PA_KERNEL_MFMA && (f32_pair || group > 16)) return PA_ERR_UNSUPPORTED;
+  if (k == PA_KERNEL_MFMA_PERSIST && num_seqs > pa::kPersistMaxSeqs) k = PA_KERNEL_MFMA;
+  if ((k == PA_KERNEL_MFMA || k == PA_KERNEL_MFMA_PERSIST) && (f32_pair || group > 16)) return PA_ERR_UNSUPPORTED;
   if (k == PA_KERNEL_VALU && group > 8) return PA_ERR_UNSUPPORTED;
   Workspace ws;
   if (!workspace_layout(num_seqs, num_q_heads, cache->head_dim, max_context_len, P, &ws)) return PA_ERR_SHAPE;
@@ -107,9 +112,9 @@ pa_status prepare_decode(const void* q, int32_t q_dtype, int32_t num_seqs, int32
   a.block_tables = block_tables;
   a.context_lens = context_lens;
   uint8_t* wsb = static_cast<uint8_t*>(workspace);
-  a.ws_m = ws.bytes ? reinterpret_cast<float*>(wsb + ws.m_off) : nullptr;
-  a.ws_l = ws.bytes ? reinterpret_cast<float*>(wsb + ws.l_off) : nullptr;
-  a.ws_o = ws.bytes ? reinterpret_cast<float*>(wsb + ws.o_off) : nullptr;
+  a.ws_m = ws.parts > 1 ? reinterpret_cast<float*>(wsb + ws.m_off) : nullptr;
+  a.ws_l = ws.parts > 1 ? reinterpret_cast<float*>(wsb + ws.l_off) : nullptr;
+  a.ws_o = ws.parts > 1 ? reinterpret_cast<float*>(wsb + ws.o_off) : nullptr;
   a.out = out;
   a.row_bytes = (int64_t)cache->num_kv_heads * cache->head_dim * esz;
   a.block_bytes = a.row_bytes * cache->block_size;
@@ -123,13 +128,16 @@ pa_status prepare_decode(const void* q, int32_t q_dtype, int32_t num_seqs, int32
   a.bt_stride = max_blocks_per_seq;
   a.max_parts = ws.parts;
   a.partition_tokens = P;
-  a.heads_per_wg = cache->num_kv_heads % 4 == 0 ? 4 : cache->num_kv_heads % 2 == 0 ? 2 : 1;
+  a.heads_per_wg = 1;
+  for (int32_t h = PA_MAX_HEADS_PER_WG; h > 1; h /= 2)
+    if (cache->num_kv_heads % h == 0 && (k == PA_KERNEL_MFMA || h <= 4)) { a.heads_per_wg = h; break; }
   a.head_groups = cache->num_kv_heads / a.heads_per_wg;
   a.q_fmt = q_dtype;
   a.kv_fmt = cache->dtype;
   const float ks = cache->dtype == PA_FP8_E4M3 ? cache->k_scale : 1.0f;
   a.qk_scale = scale * kLog2e * ks;
   a.v_scale = cache->dtype == PA_FP8_E4M3 ? cache->v_scale : 1.0f;
+  a.dense = num_seqs <= pa::kDenseMaxSeqs && (int64_t)ws.parts * a.head_groups * num_seqs < INT32_MAX;
   call->kernel = k;
   call->ws = ws;
   return PA_OK;
@@ -138,8 +146,9 @@ pa_status prepare_decode(const void* q, int32_t q_dtype, int32_t num_seqs, int32
 pa_status run_partition(const DecodeCall& c, void* stream) {
   if (c.args.num_seqs == 0) return PA_OK;
   const hipStream_t s = static_cast<hipStream_t>(stream);
-  const hipError_t e = c.kernel == PA_KERNEL_MFMA ? pa::launch_decode_mfma(c.args, s)
-                                                  : pa::launch_decode_valu(c.args, s);
+  const hipError_t e = c.kernel == PA_KERNEL_MFMA_PERSIST ? pa::launch_decode_persist(c.args, s)
+                       : c.kernel == PA_KERNEL_MFMA         ? pa::launch_decode_mfma(c.args, s)
+                                                            : pa::launch_decode_valu(c.args, s);
   return e == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 

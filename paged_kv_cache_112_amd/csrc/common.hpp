@@ -102,4 +102,62 @@ __device__ __forceinline__ float wave_max(float x) {
 
 __device__ __forceinline__ float wave_sum(float x) { return group_sum<64>(x); }
 
+// -- dense numbering of (sequence, partition) pairs -------------------------------
+// Sequence b has F_b = floor(ctx_b / P) full partitions and, when P does not divide
+// ctx_b (or ctx_b is 0), one shorter last partition.  Pairs are numbered longest
+// first: every full partition (sequence by sequence), then every shorter one, so the
+// last workgroups handed out are the short ones.  Every lane of the wave gets pair
+// x's sequence, partition and context length; returns false when x is past the last
+// pair.  All context lengths are loaded at once (up to kDenseMaxSeqs sequences).
+constexpr int kDenseMaxSeqs = 1024;
+
+// inclusive prefix sum over the wave
+__device__ __forceinline__ int wave_scan(int v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(v, d);
+    if (lane >= d) v += y;
+  }
+  return v;
+}
+
+__device__ __forceinline__ bool locate_partition(const int32_t* __restrict__ context_lens, int B, int P, int x,
+                                                 int& b_out, int& part_out, int& ctx_out) {
+  constexpr int NC = kDenseMaxSeqs / 64;
+  const int lane = threadIdx.x & 63;
+  int cx[NC];
+#pragma unroll
+  for (int k = 0; k < NC; ++k) {
+    const int i = 64 * k + lane;
+    cx[k] = -1;
+    if (64 * k < B && i < B) cx[k] = context_lens[i];
+  }
+  // pass 0: full partitions; pass 1: the shorter last partitions
+#pragma unroll
+  for (int pass = 0; pass < 2; ++pass) {
+    int base = 0;
+#pragma unroll
+    for (int k = 0; k < NC; ++k) {
+      if (64 * k >= B) break;
+      const int c = cx[k];
+      const int n = c < 0 ? 0 : pass == 0 ? c / P : ((c % P) != 0 || c == 0 ? 1 : 0);
+      const int incl = wave_scan(n) + base;
+      const int tot = __shfl(incl, 63);
+      if (x < tot) {
+        const unsigned long long m = __ballot(incl > x);
+        const int l = __ffsll((long long)m) - 1;
+        const int cl = __shfl(c, l);
+        b_out = __builtin_amdgcn_readfirstlane(64 * k + l);
+        part_out = __builtin_amdgcn_readfirstlane(pass == 0 ? x - __shfl(incl - n, l) : cl / P);
+        ctx_out = __builtin_amdgcn_readfirstlane(cl);
+        return true;
+      }
+      base = tot;
+    }
+    x -= base;
+  }
+  return false;
+}
+
 }  // namespace pa

@@ -33,63 +33,48 @@
 // Tokens past the context are clamped to the last valid row for addressing (no
 // stray or out-of-range reads, never a table entry past the context) and given
 // probability 0.
-#include <type_traits>
-
-#include "common.hpp"
 #include "launch.hpp"
+#include "mfma_tiles.hpp"
+
+#ifndef PA_MFMA_DEPTH
+#define PA_MFMA_DEPTH 3   // K or V tiles in flight per wave
+#endif
+#ifndef PA_NT_LOADS
+#define PA_NT_LOADS 0     // 1: K/V tiles loaded with the non-temporal hint (read-once data)
+#endif
+#ifndef PA_MIN_WAVES_PER_EU
+#define PA_MIN_WAVES_PER_EU 1
+#endif
+#ifndef PA_WG_THREADS
+#define PA_WG_THREADS 256
+#endif
 
 namespace pa {
 
-template <bool FP8, int D>
-struct KTile {
-  static constexpr int N = FP8 ? D / 64 : D / 32;   // 16-byte loads per lane
-  u32x4 w[N];
-};
-
-template <bool FP8, int D>
-struct VTile {
-  // bytes per lane per row: VEC elements, VEC = D / 16
-  static constexpr int BYTES = (D / 16) * (FP8 ? 1 : 2);
-  typedef typename std::conditional<BYTES == 16, u32x4, typename std::conditional<BYTES == 8, u32x2, uint32_t>::type>::type W;
-  W w[4];
-};
-
-template <bool FP8, int D>
-__device__ __forceinline__ int q_col(int kk, int q4) {
-  if constexpr (FP8) {
-    if constexpr (D == 128) return 64 * (kk >> 1) + 16 * q4 + 8 * (kk & 1);
-    else return 16 * q4 + 8 * kk;
-  } else {
-    return 32 * kk + 8 * q4;
-  }
-}
-
-// Eight E4M3 bytes (two words) to a bf16x8 MFMA operand, element order preserved.
-__device__ __forceinline__ bf16x8 e4m3x8_to_bf16x8(uint32_t w0, uint32_t w1) {
-  u32x4 r;
-  r[0] = e4m3x2_to_bf16x2(e4m3x2_lo(w0));
-  r[1] = e4m3x2_to_bf16x2(e4m3x2_hi(w0));
-  r[2] = e4m3x2_to_bf16x2(e4m3x2_lo(w1));
-  r[3] = e4m3x2_to_bf16x2(e4m3x2_hi(w1));
-  return __builtin_bit_cast(bf16x8, r);
-}
-
 template <bool FP8, int D, int PT>
-__global__ __launch_bounds__(256) void decode_mfma_kernel(const DecodeArgs a) {
+__global__ __launch_bounds__(PA_WG_THREADS) __attribute__((amdgpu_waves_per_eu(PA_MIN_WAVES_PER_EU, 8)))
+void decode_mfma_kernel(const DecodeArgs a) {
   constexpr int P = 16 * PT;
   constexpr int ESZ = FP8 ? 1 : 2;
   constexpr int VEC = D / 16;
   constexpr int NKK = D / 32;
-  constexpr int DEPTH = 3;
+  constexpr int DEPTH = PA_MFMA_DEPTH;
   constexpr int KD = PT < DEPTH ? PT : DEPTH;
   __shared__ int32_t tbl[P];
 
-  const int b = blockIdx.y;
-  const int part = blockIdx.x / a.head_groups;
-  const int hg = blockIdx.x - part * a.head_groups;
-  const int ctx = a.context_lens[b];
-  const int t0 = part * P;
-  if (t0 >= ctx && !(part == 0 && ctx == 0)) return;          // same for the whole workgroup
+  const int hg = blockIdx.x % a.head_groups;
+  int b, part, ctx;
+  if (a.dense) {
+    // workgroup x / head_groups is the x-th existing (sequence, partition) pair;
+    // the grid's surplus workgroups come last and leave at once
+    if (!locate_partition(a.context_lens, a.num_seqs, P, blockIdx.x / a.head_groups, b, part, ctx)) return;
+  } else {
+    b = blockIdx.y;
+    part = blockIdx.x / a.head_groups;
+    ctx = a.context_lens[b];
+    if (part * P >= ctx && !(part == 0 && ctx == 0)) return;
+  }
+  const int t0 = part * P;          // same for the whole workgroup
 
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
@@ -141,7 +126,10 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(const DecodeArgs a) {
     KTile<FP8, D> t;
     const uint8_t* p = kbase + row_off(t0 + 16 * i + n) + 16 * q4;
 #pragma unroll
-    for (int j = 0; j < KTile<FP8, D>::N; ++j) t.w[j] = ld16(p + 64 * j);
+    for (int j = 0; j < KTile<FP8, D>::N; ++j) {
+      if constexpr (PA_NT_LOADS) t.w[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p + 64 * j));
+      else t.w[j] = ld16(p + 64 * j);
+    }
     return t;
   };
   auto load_v = [&](int i) {
@@ -149,7 +137,8 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(const DecodeArgs a) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const uint8_t* p = vbase + row_off(t0 + 16 * i + 4 * q4 + j) + n * VEC * ESZ;
-      t.w[j] = *reinterpret_cast<const typename VTile<FP8, D>::W*>(p);
+      if constexpr (PA_NT_LOADS) t.w[j] = __builtin_nontemporal_load(reinterpret_cast<const typename VTile<FP8, D>::W*>(p));
+      else t.w[j] = *reinterpret_cast<const typename VTile<FP8, D>::W*>(p);
     }
     return t;
   };
@@ -163,18 +152,7 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(const DecodeArgs a) {
   for (int i = 0; i < PT; ++i) {
     const KTile<FP8, D> cur = kt[i % KD];
     if (i + KD < PT) kt[i % KD] = load_k(i + KD);
-    f32x4 s = {0.f, 0.f, 0.f, 0.f};
-    if constexpr (!FP8) {
-#pragma unroll
-      for (int kk = 0; kk < NKK; ++kk)
-        s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, cur.w[kk]), qB[kk], s, 0, 0, 0);
-    } else {
-#pragma unroll
-      for (int h = 0; h < KTile<FP8, D>::N; ++h) {
-        s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(e4m3x8_to_bf16x8(cur.w[h][0], cur.w[h][1]), qB[2 * h], s, 0, 0, 0);
-        s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(e4m3x8_to_bf16x8(cur.w[h][2], cur.w[h][3]), qB[2 * h + 1], s, 0, 0, 0);
-      }
-    }
+    const f32x4 s = qk_tile<FP8, D>(cur, qB);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int tok = t0 + 16 * i + 4 * q4 + r;
@@ -220,37 +198,7 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(const DecodeArgs a) {
   for (int i = 0; i < PT; ++i) {
     const VTile<FP8, D> cur = vt[i % KD];
     if (i + KD < PT) vt[i % KD] = load_v(i + KD);
-    const bf16x4 A = __builtin_bit_cast(bf16x4, u32x2{Pk[i][0], Pk[i][1]});
-    // per row j: VEC/2 words of bf16 pairs (elements 2c, 2c+1)
-    uint32_t rw[4][VEC / 2];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      if constexpr (!FP8) {
-#pragma unroll
-        for (int c = 0; c < VEC / 2; ++c) {
-          if constexpr (VEC / 2 == 4) rw[j][c] = cur.w[j][c];
-          else if constexpr (VEC / 2 == 2) rw[j][c] = cur.w[j][c];
-          else rw[j][c] = cur.w[j];
-        }
-      } else {
-        if constexpr (VEC == 8) {
-          rw[j][0] = e4m3x2_to_bf16x2(e4m3x2_lo(cur.w[j][0]));
-          rw[j][1] = e4m3x2_to_bf16x2(e4m3x2_hi(cur.w[j][0]));
-          rw[j][2] = e4m3x2_to_bf16x2(e4m3x2_lo(cur.w[j][1]));
-          rw[j][3] = e4m3x2_to_bf16x2(e4m3x2_hi(cur.w[j][1]));
-        } else {
-          rw[j][0] = e4m3x2_to_bf16x2(e4m3x2_lo(cur.w[j]));
-          rw[j][1] = e4m3x2_to_bf16x2(e4m3x2_hi(cur.w[j]));
-        }
-      }
-    }
-#pragma unroll
-    for (int c = 0; c < VEC / 2; ++c) {
-      const u32x2 even = {pack_lo_halves(rw[0][c], rw[1][c]), pack_lo_halves(rw[2][c], rw[3][c])};
-      const u32x2 odd = {pack_hi_halves(rw[0][c], rw[1][c]), pack_hi_halves(rw[2][c], rw[3][c])};
-      O[2 * c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(A, __builtin_bit_cast(bf16x4, even), O[2 * c], 0, 0, 0);
-      O[2 * c + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(A, __builtin_bit_cast(bf16x4, odd), O[2 * c + 1], 0, 0, 0);
-    }
+    pv_tile<FP8, D>(cur, Pk[i][0], Pk[i][1], O);
   }
 
   // ---- write: lane (n, q4) register r holds O[g = 4*q4 + r][d = VEC*n + e] --------
@@ -301,7 +249,8 @@ static hipError_t launch_pt(const DecodeArgs& a, dim3 grid, dim3 block, hipStrea
 }
 
 hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t s) {
-  const dim3 grid((unsigned)(a.max_parts * a.head_groups), (unsigned)a.num_seqs);
+  const dim3 grid = a.dense ? dim3((unsigned)(a.max_parts * a.head_groups * a.num_seqs), 1u)
+                           : dim3((unsigned)(a.max_parts * a.head_groups), (unsigned)a.num_seqs);
   const dim3 block((unsigned)(kWave * a.heads_per_wg));
   const bool fp8 = a.kv_fmt == kE4m3;
   if (a.head_dim == 128) return fp8 ? launch_pt<true, 128>(a, grid, block, s) : launch_pt<false, 128>(a, grid, block, s);

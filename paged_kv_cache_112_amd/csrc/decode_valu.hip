@@ -60,12 +60,19 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(const DecodeArgs a) {
   __shared__ int32_t tbl[PMAX];
 
   const int P = a.partition_tokens;
-  const int b = blockIdx.y;
-  const int part = blockIdx.x / a.head_groups;
-  const int hg = blockIdx.x - part * a.head_groups;
-  const int ctx = a.context_lens[b];
+  const int hg = blockIdx.x % a.head_groups;
+  int b, part, ctx;
+  if (a.dense) {
+    // workgroup x / head_groups is the x-th existing (sequence, partition) pair;
+    // the grid's surplus workgroups come last and leave at once
+    if (!locate_partition(a.context_lens, a.num_seqs, P, blockIdx.x / a.head_groups, b, part, ctx)) return;
+  } else {
+    b = blockIdx.y;
+    part = blockIdx.x / a.head_groups;
+    ctx = a.context_lens[b];
+    if (part * P >= ctx && !(part == 0 && ctx == 0)) return;
+  }
   const int t0 = part * P;
-  if (t0 >= ctx && !(part == 0 && ctx == 0)) return;
 
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
@@ -218,7 +225,8 @@ static hipError_t launch_d(const DecodeArgs& a, dim3 grid, dim3 block, hipStream
 }
 
 hipError_t launch_decode_valu(const DecodeArgs& a, hipStream_t s) {
-  const dim3 grid((unsigned)(a.max_parts * a.head_groups), (unsigned)a.num_seqs);
+  const dim3 grid = a.dense ? dim3((unsigned)(a.max_parts * a.head_groups * a.num_seqs), 1u)
+                           : dim3((unsigned)(a.max_parts * a.head_groups), (unsigned)a.num_seqs);
   const dim3 block((unsigned)(kWave * a.heads_per_wg));
   if (a.kv_fmt == kF32 && a.q_fmt == kF32) return launch_d<kF32, kF32>(a, grid, block, s);
   if (a.kv_fmt == kBf16 && a.q_fmt == kBf16) return launch_d<kBf16, kBf16>(a, grid, block, s);

@@ -39,7 +39,11 @@ struct DecodeArgs {
   int32_t q_fmt, kv_fmt;
   float qk_scale;            // scale * log2(e) * k_scale
   float v_scale;
+  int32_t dense;             // 1: workgroup ids number only existing (sequence, partition) pairs
 };
+
+// Largest batch the persistent kernel takes (its per-workgroup running total lives in LDS).
+constexpr int kPersistMaxSeqs = 1024;
 
 struct MergeArgs {
   const float* ws_m;
@@ -52,6 +56,7 @@ struct MergeArgs {
 
 hipError_t launch_write_kv(const WriteArgs& a, hipStream_t stream);
 hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_decode_persist(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_decode_valu(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t stream);
 

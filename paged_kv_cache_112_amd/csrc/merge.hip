@@ -7,7 +7,9 @@
 // over the sequence dimension and the pieces reduced afterwards; the rescaling
 // is the running-max correction of its online softmax).  Sequences that fit in
 // one partition were finished by the partition kernel and are skipped here.
-// One wave per (query head, sequence); lanes own head_dim / 64 output columns.
+// One wave per (query head, sequence): four groups of 16 lanes each take every
+// fourth partition, each lane owning head_dim / 16 columns; the groups are summed
+// with cross-lane adds at the end.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -15,17 +17,20 @@ namespace pa {
 
 template <int D, int OF>
 __global__ __launch_bounds__(64) void merge_kernel(const MergeArgs a) {
-  constexpr int DPL = D / kWave;
+  // lane = (partition slot pg in 0..3, column group dl in 0..15); each lane owns D/16 columns
+  constexpr int DPL = D / 16;
   const int h = blockIdx.x;
   const int b = blockIdx.y;
   const int lane = threadIdx.x;
+  const int pg = lane >> 4;
+  const int d0 = (lane & 15) * DPL;
   const int ctx = a.context_lens[b];
   const int n = (ctx + a.partition_tokens - 1) / a.partition_tokens;
   if (n <= 1) return;
   const int64_t base = ((int64_t)b * a.num_q_heads + h) * a.max_parts;
   const float* ms = a.ws_m + base;
   const float* ls = a.ws_l + base;
-  const float* os = a.ws_o + base * D + lane * DPL;
+  const float* os = a.ws_o + base * D + d0;
 
   float M = -INFINITY;
   for (int j = lane; j < n; j += kWave) M = fmaxf(M, ms[j]);
@@ -34,21 +39,48 @@ __global__ __launch_bounds__(64) void merge_kernel(const MergeArgs a) {
   for (int j = lane; j < n; j += kWave) L += ls[j] * __builtin_amdgcn_exp2f(ms[j] - M);
   L = wave_sum(L);
 
+  // four partitions per wave load; all loads of a round of 16 partitions are issued together
   float acc[DPL];
 #pragma unroll
   for (int i = 0; i < DPL; ++i) acc[i] = 0.f;
-  for (int j = 0; j < n; ++j) {
-    const float w = __builtin_amdgcn_exp2f(ms[j] - M);
+  for (int j0 = 0; j0 < n; j0 += 16) {
+    f32x4 ov[4][DPL / 4];
+    float wv[4];
 #pragma unroll
-    for (int i = 0; i < DPL; ++i) acc[i] = fmaf(w, os[(int64_t)j * D + i], acc[i]);
+    for (int u = 0; u < 4; ++u) {
+      const int j = j0 + 4 * u + pg;
+      const int jc = min(j, n - 1);
+      wv[u] = j < n ? __builtin_amdgcn_exp2f(ms[jc] - M) : 0.f;
+#pragma unroll
+      for (int c = 0; c < DPL / 4; ++c) ov[u][c] = __builtin_bit_cast(f32x4, ld16(os + (int64_t)jc * D + 4 * c));
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int c = 0; c < DPL / 4; ++c)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[4 * c + e] = fmaf(wv[u], ov[u][c][e], acc[4 * c + e]);
   }
-  const float inv = 1.0f / L;
-  const int64_t o = ((int64_t)b * a.num_q_heads + h) * D + lane * DPL;
 #pragma unroll
   for (int i = 0; i < DPL; ++i) {
-    const float y = acc[i] * inv;
-    if constexpr (OF == kF32) static_cast<float*>(a.out)[o + i] = y;
-    else static_cast<uint16_t*>(a.out)[o + i] = __builtin_bit_cast(uint16_t, (__bf16)y);
+    acc[i] += __shfl_xor(acc[i], 16);
+    acc[i] += __shfl_xor(acc[i], 32);
+  }
+  if (pg != 0) return;
+  const float inv = 1.0f / L;
+  const int64_t o = ((int64_t)b * a.num_q_heads + h) * D + d0;
+  if constexpr (OF == kF32) {
+#pragma unroll
+    for (int c = 0; c < DPL / 4; ++c)
+      st16(static_cast<float*>(a.out) + o + 4 * c,
+           __builtin_bit_cast(u32x4, f32x4{acc[4 * c], acc[4 * c + 1], acc[4 * c + 2], acc[4 * c + 3]} * inv));
+  } else {
+    uint32_t wds[DPL / 2];
+#pragma unroll
+    for (int c = 0; c < DPL / 2; ++c) wds[c] = pack_bf16(acc[2 * c] * inv, acc[2 * c + 1] * inv);
+    uint16_t* dst = static_cast<uint16_t*>(a.out) + o;
+    if constexpr (DPL == 8) st16(dst, u32x4{wds[0], wds[1], wds[2], wds[3]});
+    else st8(dst, u32x2{wds[0], wds[1]});
   }
 }
 

@@ -39,7 +39,7 @@ def test_status_strings():
 def test_workspace_bytes():
     # one partition: no workspace
     assert pa.pa_decode_workspace_bytes(64, 32, 128, 256, 0) == 0
-    # cfg2-sized: J = ceil(3360/256) = 14
+    # the Llama-3-8B batch-64 shape: J = ceil(3360/256) = 14
     rows = 64 * 32 * 14
     al = lambda x: (x + 255) // 256 * 256
     assert pa.pa_decode_workspace_bytes(64, 32, 128, 3360, 0) == 2 * al(rows * 4) + al(rows * 128 * 4)
@@ -78,6 +78,7 @@ def _decode(**kw):
     (dict(partition_tokens=100), pa.PA_ERR_UNSUPPORTED),
     (dict(kernel=pa.PA_KERNEL_MFMA), pa.PA_ERR_UNSUPPORTED),            # f32 has no matrix-core path
     (dict(kernel=9), pa.PA_ERR_UNSUPPORTED),
+    (dict(kernel=pa.PA_KERNEL_MFMA_PERSIST), pa.PA_ERR_UNSUPPORTED),
     (dict(num_q_heads=32, cache=_cache(num_kv_heads=2), kernel=pa.PA_KERNEL_VALU), pa.PA_ERR_UNSUPPORTED),
     (dict(workspace=None, partition_tokens=16), pa.PA_ERR_WORKSPACE),
     (dict(workspace_bytes=100, partition_tokens=16), pa.PA_ERR_WORKSPACE),

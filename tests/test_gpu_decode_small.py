@@ -13,7 +13,7 @@ from workloads import make_config
 pytestmark = pytest.mark.gpu
 
 TOL = {"f32": 1e-5, "bf16": 2e-2, "e4m3": 2e-2}
-KERNELS = {"valu": 1, "mfma": 2}
+KERNELS = {"valu": 1, "mfma": 2, "persist": 3}
 
 
 def _check(dev, w, partition_tokens=0, kernel=0, tol=None, scale=None):
@@ -58,7 +58,8 @@ EDGE_CTX = [1, 2, 15, 16, 17, 31, 255, 256, 257, 300, 511, 513, 0, 64]
 
 
 @pytest.mark.parametrize("kv,q,kernel", [("f32", "f32", "valu"), ("bf16", "bf16", "mfma"), ("bf16", "bf16", "valu"),
-                                         ("e4m3", "bf16", "mfma"), ("e4m3", "bf16", "valu")])
+                                         ("bf16", "bf16", "persist"), ("e4m3", "bf16", "mfma"), ("e4m3", "bf16", "valu"),
+                                         ("e4m3", "bf16", "persist")])
 @pytest.mark.parametrize("hq,hkv,d", [(32, 8, 128), (8, 8, 64), (16, 2, 128)])
 @pytest.mark.parametrize("P", [0, 64])
 def test_edge_lengths(kv, q, kernel, hq, hkv, d, P):
@@ -67,7 +68,7 @@ def test_edge_lengths(kv, q, kernel, hq, hkv, d, P):
 
 
 @pytest.mark.parametrize("bs", [1, 2, 8, 64, 256])
-@pytest.mark.parametrize("kv,kernel", [("bf16", "mfma"), ("f32", "valu"), ("e4m3", "mfma")])
+@pytest.mark.parametrize("kv,kernel", [("bf16", "mfma"), ("f32", "valu"), ("e4m3", "mfma"), ("bf16", "persist")])
 def test_block_sizes(bs, kv, kernel):
     w = custom_workload([300, 1, 47, 129], 8, 2, 128, bs, kv, "f32" if kv == "f32" else "bf16", seed=bs)
     _check(DeviceInputs(build_host_inputs(w)), w, partition_tokens=64, kernel=KERNELS[kernel])
@@ -132,7 +133,7 @@ def test_peaky_softmax(kv, kernel):
 # ---------------------------------------------------------------------------
 # invariances (bitwise on the GPU: reduction order depends on logical positions only)
 # ---------------------------------------------------------------------------
-@pytest.mark.parametrize("kv,kernel", [("bf16", 2), ("f32", 1), ("e4m3", 2)])
+@pytest.mark.parametrize("kv,kernel", [("bf16", 2), ("f32", 1), ("e4m3", 2), ("bf16", 3)])
 def test_bitwise_invariant_under_placement_and_block_size(kv, kernel):
     q = "f32" if kv == "f32" else "bf16"
     outs = []
@@ -141,6 +142,42 @@ def test_bitwise_invariant_under_placement_and_block_size(kv, kernel):
         outs.append(from_dev(DeviceInputs(build_host_inputs(w)).decode(partition_tokens=128, kernel=kernel)))
     for o in outs[1:]:
         assert np.array_equal(o.view(np.uint8), outs[0].view(np.uint8))
+
+
+@pytest.mark.parametrize("P", [16, 64, 128])
+def test_persistent_and_grid_kernels_agree_bitwise(P):
+    """Both matrix-core schedules compute each partition in the same order: identical bits."""
+    w = custom_workload(EDGE_CTX + [1000, 2047], 32, 8, 128, 16, "bf16", "bf16", seed=41)
+    dev = DeviceInputs(build_host_inputs(w))
+    a = from_dev(dev.decode(partition_tokens=P, kernel=2))
+    b = from_dev(dev.decode(partition_tokens=P, kernel=3))
+    assert np.array_equal(a, b)
+
+
+def test_repeated_calls_on_one_workspace():
+    """Repeated calls on one workspace give identical results."""
+    import torch
+    import paged_kv_cache_112_amd as pa
+    w = custom_workload([300, 17, 1500, 64, 0, 999], 32, 8, 128, 16, "bf16", "bf16", seed=43)
+    h = build_host_inputs(w)
+    dev = DeviceInputs(h)
+    ws = pa.new_workspace(w.num_seqs, 32, 128, dev.max_ctx, 64)
+    outs = []
+    for _ in range(4):
+        res = pa.decode(dev.q, dev.kc, dev.vc, dev.bt, dev.ctx, w.scale, max_context_len=dev.max_ctx,
+                        workspace=ws, partition_tokens=64, kernel=3)
+        torch.cuda.synchronize()
+        outs.append(from_dev(res))
+    for o in outs[1:]:
+        assert np.array_equal(o, outs[0])
+    assert np.abs(out_to_f64(res) - h.oracle_decode()).max() <= 2e-2
+
+
+def test_large_batch_falls_back_to_grid_kernel():
+    """More sequences than the persistent kernel's running total holds: the grid kernel runs instead."""
+    ctx = [1 + (7 * i) % 90 for i in range(1100)]
+    w = custom_workload(ctx, 8, 2, 64, 16, "bf16", "bf16", seed=47)
+    _check(DeviceInputs(build_host_inputs(w)), w, partition_tokens=32, kernel=3)
 
 
 # ---------------------------------------------------------------------------
