@@ -111,14 +111,21 @@ __device__ __forceinline__ float wave_sum(float x) { return group_sum<64>(x); }
 // pair.  All context lengths are loaded at once (up to kDenseMaxSeqs sequences).
 constexpr int kDenseMaxSeqs = 1024;
 
-// inclusive prefix sum over the wave
+// Inclusive prefix sum over the wave, on DPP: shifts right by 1, 2, 4 and 8 lanes
+// within each 16-lane row (lanes shifted in from outside the row add 0), then
+// row_bcast:15 adds the last lane of rows 0 and 2 to rows 1 and 3, and row_bcast:31
+// adds lane 31 to rows 2 and 3.
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ int dpp_or_zero(int x) {
+  return __builtin_amdgcn_update_dpp(0, x, CTRL, ROW_MASK, 0xf, false);
+}
 __device__ __forceinline__ int wave_scan(int v) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int y = __shfl_up(v, d);
-    if (lane >= d) v += y;
-  }
+  v += dpp_or_zero<0x111>(v);        // row_shr:1
+  v += dpp_or_zero<0x112>(v);        // row_shr:2
+  v += dpp_or_zero<0x114>(v);        // row_shr:4
+  v += dpp_or_zero<0x118>(v);        // row_shr:8
+  v += dpp_or_zero<0x142, 0xa>(v);   // row_bcast:15 into rows 1 and 3
+  v += dpp_or_zero<0x143, 0xc>(v);   // row_bcast:31 into rows 2 and 3
   return v;
 }
 
@@ -126,6 +133,7 @@ __device__ __forceinline__ bool locate_partition(const int32_t* __restrict__ con
                                                  int& b_out, int& part_out, int& ctx_out) {
   constexpr int NC = kDenseMaxSeqs / 64;
   const int lane = threadIdx.x & 63;
+  const int log2p = __builtin_ctz((unsigned)P);   // P is a power of two
   int cx[NC];
 #pragma unroll
   for (int k = 0; k < NC; ++k) {
@@ -141,16 +149,19 @@ __device__ __forceinline__ bool locate_partition(const int32_t* __restrict__ con
     for (int k = 0; k < NC; ++k) {
       if (64 * k >= B) break;
       const int c = cx[k];
-      const int n = c < 0 ? 0 : pass == 0 ? c / P : ((c % P) != 0 || c == 0 ? 1 : 0);
+      const int n = c < 0 ? 0 : pass == 0 ? c >> log2p : ((c & (P - 1)) != 0 || c == 0 ? 1 : 0);
       const int incl = wave_scan(n) + base;
-      const int tot = __shfl(incl, 63);
+      const int tot = __builtin_amdgcn_readlane(incl, 63);
       if (x < tot) {
         const unsigned long long m = __ballot(incl > x);
-        const int l = __ffsll((long long)m) - 1;
-        const int cl = __shfl(c, l);
-        b_out = __builtin_amdgcn_readfirstlane(64 * k + l);
-        part_out = __builtin_amdgcn_readfirstlane(pass == 0 ? x - __shfl(incl - n, l) : cl / P);
-        ctx_out = __builtin_amdgcn_readfirstlane(cl);
+        const int l = __builtin_amdgcn_readfirstlane(__ffsll((long long)m) - 1);
+        const int b = 64 * k + l;
+        const int cl = __builtin_amdgcn_readlane(c, l);
+        // a pair always belongs to a real sequence with 0 <= ctx; anything else is refused
+        if (l < 0 || b >= B || cl < 0) return false;
+        b_out = b;
+        part_out = pass == 0 ? x - __builtin_amdgcn_readlane(incl - n, l) : cl >> log2p;
+        ctx_out = cl;
         return true;
       }
       base = tot;

@@ -51,7 +51,17 @@
 
 namespace pa {
 
-template <bool FP8, int D, int PT>
+// A uniform load through the scalar data cache (read only).
+__device__ __forceinline__ int32_t load_uniform(const int32_t* p) {
+  return *(const __attribute__((address_space(4))) int32_t*)p;
+}
+
+// Query head g of the group sits in MFMA column n = 4 * (g % 4) + g / 4, so that
+// after P.V lane (n, q4) register r holds head 4 * r + q4: with G <= 4 every lane
+// of the wave holds one head's output in register 0.
+__device__ __forceinline__ int head_of_column(int n) { return 4 * (n & 3) + (n >> 2); }
+
+template <bool FP8, int D, int PT, bool BIGBS>
 __global__ __launch_bounds__(PA_WG_THREADS) __attribute__((amdgpu_waves_per_eu(PA_MIN_WAVES_PER_EU, 8)))
 void decode_mfma_kernel(const DecodeArgs a) {
   constexpr int P = 16 * PT;
@@ -60,7 +70,7 @@ void decode_mfma_kernel(const DecodeArgs a) {
   constexpr int NKK = D / 32;
   constexpr int DEPTH = PA_MFMA_DEPTH;
   constexpr int KD = PT < DEPTH ? PT : DEPTH;
-  __shared__ int32_t tbl[P];
+  __shared__ int32_t tbl[BIGBS ? 1 : P];
 
   const int hg = blockIdx.x % a.head_groups;
   int b, part, ctx;
@@ -91,12 +101,15 @@ void decode_mfma_kernel(const DecodeArgs a) {
     return;
   }
 
-  const int n_tok = min(P, ctx - t0);
   const int lb0 = t0 >> a.log2_bs;
-  const int n_ent = ((t0 + n_tok - 1) >> a.log2_bs) - lb0 + 1;
   const int32_t* bt_row = a.block_tables + (int64_t)b * a.bt_stride + lb0;
-  for (int i = threadIdx.x; i < n_ent; i += blockDim.x) tbl[i] = bt_row[i];
-  __syncthreads();
+  if constexpr (!BIGBS) {
+    // blocks shorter than a tile: stage the partition's table entries in LDS
+    const int n_tok = min(P, ctx - t0);
+    const int n_ent = ((t0 + n_tok - 1) >> a.log2_bs) - lb0 + 1;
+    for (int i = threadIdx.x; i < n_ent; i += blockDim.x) tbl[i] = bt_row[i];
+    __syncthreads();
+  }
 
   const int64_t head_off = (int64_t)kvh * D * ESZ;
   const uint8_t* kbase = a.k_cache + head_off;
@@ -104,27 +117,42 @@ void decode_mfma_kernel(const DecodeArgs a) {
   const int bs_mask = a.block_size - 1;
   const int log2bs = a.log2_bs;
   const int64_t block_bytes = a.block_bytes, row_bytes = a.row_bytes;
+  // Byte offset of token t (clamped to the last valid one) within the pool.  With
+  // blocks of 16 tokens or more a tile lies in one block (tiles are 16-aligned), so
+  // its block id is uniform and comes from the scalar cache; tiles past the context
+  // clamp to the block of token ctx - 1.
+  int32_t tile_blk[BIGBS ? PT : 1];
+  if constexpr (BIGBS) {
+#pragma unroll
+    for (int i = 0; i < PT; ++i) tile_blk[i] = load_uniform(bt_row + ((min(t0 + 16 * i, ctx - 1) >> log2bs) - lb0));
+  }
+  auto tile_block = [&](int i) -> int64_t { return (int64_t)tile_blk[i] * block_bytes; };
   auto row_off = [&](int t) -> int64_t {
     const int tc = min(t, ctx - 1);
     const int blk = tbl[(tc >> log2bs) - lb0];
     return (int64_t)blk * block_bytes + (int64_t)(tc & bs_mask) * row_bytes;
   };
+  auto lane_row = [&](int t) -> int64_t { return (int64_t)(min(t, ctx - 1) & bs_mask) * row_bytes; };
 
-  // q^T as the B operand of q.K^T: lane (n = query head in group, q4) holds 8 d's per MFMA
+  // q^T as the B operand of q.K^T: lane (n, q4) holds 8 d's of head head_of_column(n)
   bf16x8 qB[NKK];
   {
-    const uint16_t* qrow = static_cast<const uint16_t*>(a.q) + ((int64_t)b * a.num_q_heads + hq0 + n) * D;
+    const int g = head_of_column(n);
+    const uint16_t* qrow = static_cast<const uint16_t*>(a.q) + ((int64_t)b * a.num_q_heads + hq0 + min(g, G - 1)) * D;
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
       u32x4 w = {0u, 0u, 0u, 0u};
-      if (n < G) w = ld16(qrow + q_col<FP8, D>(kk, q4));
+      if (g < G) w = ld16(qrow + q_col<FP8, D>(kk, q4));
       qB[kk] = __builtin_bit_cast(bf16x8, w);
     }
   }
 
   auto load_k = [&](int i) {
     KTile<FP8, D> t;
-    const uint8_t* p = kbase + row_off(t0 + 16 * i + n) + 16 * q4;
+    const int tok = t0 + 16 * i + n;
+    const uint8_t* p;
+    if constexpr (BIGBS) p = kbase + tile_block(i) + lane_row(tok) + 16 * q4;
+    else p = kbase + row_off(tok) + 16 * q4;
 #pragma unroll
     for (int j = 0; j < KTile<FP8, D>::N; ++j) {
       if constexpr (PA_NT_LOADS) t.w[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p + 64 * j));
@@ -134,9 +162,14 @@ void decode_mfma_kernel(const DecodeArgs a) {
   };
   auto load_v = [&](int i) {
     VTile<FP8, D> t;
+    int64_t tb = 0;
+    if constexpr (BIGBS) tb = tile_block(i);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const uint8_t* p = vbase + row_off(t0 + 16 * i + 4 * q4 + j) + n * VEC * ESZ;
+      const int tok = t0 + 16 * i + 4 * q4 + j;
+      const uint8_t* p;
+      if constexpr (BIGBS) p = vbase + tb + lane_row(tok) + n * VEC * ESZ;
+      else p = vbase + row_off(tok) + n * VEC * ESZ;
       if constexpr (PA_NT_LOADS) t.w[j] = __builtin_nontemporal_load(reinterpret_cast<const typename VTile<FP8, D>::W*>(p));
       else t.w[j] = *reinterpret_cast<const typename VTile<FP8, D>::W*>(p);
     }
@@ -144,14 +177,18 @@ void decode_mfma_kernel(const DecodeArgs a) {
   };
 
   // ---- phase 1: logits of all tiles (base 2, masked) ----------------------------
+  // The ring runs on into V: as the last K tiles are consumed, the first V tiles
+  // are already requested, so the stream of loads does not pause between phases.
   float S[PT][4];
   KTile<FP8, D> kt[KD];
+  VTile<FP8, D> vt[KD];
 #pragma unroll
   for (int i = 0; i < KD; ++i) kt[i] = load_k(i);
 #pragma unroll
   for (int i = 0; i < PT; ++i) {
     const KTile<FP8, D> cur = kt[i % KD];
     if (i + KD < PT) kt[i % KD] = load_k(i + KD);
+    else vt[i + KD - PT] = load_v(i + KD - PT);
     const f32x4 s = qk_tile<FP8, D>(cur, qB);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -160,12 +197,7 @@ void decode_mfma_kernel(const DecodeArgs a) {
     }
   }
 
-  // first V tiles in flight while the softmax runs
-  VTile<FP8, D> vt[KD];
-#pragma unroll
-  for (int i = 0; i < KD; ++i) vt[i] = load_v(i);
-
-  // ---- softmax over the partition --------------------------------------------
+  // ---- softmax over the partition (per column n, i.e. per query head) -----------
   float mx = -INFINITY;
 #pragma unroll
   for (int i = 0; i < PT; ++i)
@@ -201,12 +233,13 @@ void decode_mfma_kernel(const DecodeArgs a) {
     pv_tile<FP8, D>(cur, Pk[i][0], Pk[i][1], O);
   }
 
-  // ---- write: lane (n, q4) register r holds O[g = 4*q4 + r][d = VEC*n + e] --------
+  // ---- write: lane (n, q4) register r holds O[head 4*r + q4][d = VEC*n + e] ----------
   const bool single = ctx <= P;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
-    const int g = 4 * q4 + r;
-    const float lg = __shfl(lsum, g & 15);
+    if (4 * r >= G) break;
+    const int g = 4 * r + q4;
+    const float lg = __shfl(lsum, 4 * q4 + r);           // column of head g
     if (g < G) {
       const int64_t hrow = (int64_t)b * a.num_q_heads + hq0 + g;
       if (single) {
@@ -228,24 +261,29 @@ void decode_mfma_kernel(const DecodeArgs a) {
       }
     }
   }
-  if (!single && q4 == 0 && n < G) {
-    const int64_t idx = ((int64_t)b * a.num_q_heads + hq0 + n) * a.max_parts + part;
+  if (!single && q4 == 0 && head_of_column(n) < G) {
+    const int64_t idx = ((int64_t)b * a.num_q_heads + hq0 + head_of_column(n)) * a.max_parts + part;
     a.ws_m[idx] = mx;
     a.ws_l[idx] = lsum;
   }
 }
 
-template <bool FP8, int D>
+template <bool FP8, int D, bool BIGBS>
 static hipError_t launch_pt(const DecodeArgs& a, dim3 grid, dim3 block, hipStream_t s) {
   switch (a.partition_tokens) {
-    case 16: hipLaunchKernelGGL((decode_mfma_kernel<FP8, D, 1>), grid, block, 0, s, a); break;
-    case 32: hipLaunchKernelGGL((decode_mfma_kernel<FP8, D, 2>), grid, block, 0, s, a); break;
-    case 64: hipLaunchKernelGGL((decode_mfma_kernel<FP8, D, 4>), grid, block, 0, s, a); break;
-    case 128: hipLaunchKernelGGL((decode_mfma_kernel<FP8, D, 8>), grid, block, 0, s, a); break;
-    case 256: hipLaunchKernelGGL((decode_mfma_kernel<FP8, D, 16>), grid, block, 0, s, a); break;
+    case 16: hipLaunchKernelGGL((decode_mfma_kernel<FP8, D, 1, BIGBS>), grid, block, 0, s, a); break;
+    case 32: hipLaunchKernelGGL((decode_mfma_kernel<FP8, D, 2, BIGBS>), grid, block, 0, s, a); break;
+    case 64: hipLaunchKernelGGL((decode_mfma_kernel<FP8, D, 4, BIGBS>), grid, block, 0, s, a); break;
+    case 128: hipLaunchKernelGGL((decode_mfma_kernel<FP8, D, 8, BIGBS>), grid, block, 0, s, a); break;
+    case 256: hipLaunchKernelGGL((decode_mfma_kernel<FP8, D, 16, BIGBS>), grid, block, 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+template <bool FP8, int D>
+static hipError_t launch_bs(const DecodeArgs& a, dim3 grid, dim3 block, hipStream_t s) {
+  return a.block_size >= 16 ? launch_pt<FP8, D, true>(a, grid, block, s) : launch_pt<FP8, D, false>(a, grid, block, s);
 }
 
 hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t s) {
@@ -253,8 +291,8 @@ hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t s) {
                            : dim3((unsigned)(a.max_parts * a.head_groups), (unsigned)a.num_seqs);
   const dim3 block((unsigned)(kWave * a.heads_per_wg));
   const bool fp8 = a.kv_fmt == kE4m3;
-  if (a.head_dim == 128) return fp8 ? launch_pt<true, 128>(a, grid, block, s) : launch_pt<false, 128>(a, grid, block, s);
-  return fp8 ? launch_pt<true, 64>(a, grid, block, s) : launch_pt<false, 64>(a, grid, block, s);
+  if (a.head_dim == 128) return fp8 ? launch_bs<true, 128>(a, grid, block, s) : launch_bs<false, 128>(a, grid, block, s);
+  return fp8 ? launch_bs<true, 64>(a, grid, block, s) : launch_bs<false, 64>(a, grid, block, s);
 }
 
 }  // namespace pa
