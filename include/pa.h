@@ -148,9 +148,13 @@ typedef enum pa_kernel {
  *   out           device [num_seqs, num_q_heads, head_dim] of q_dtype
  *   workspace     device scratch of >= pa_decode_workspace_bytes(...) bytes
  *                 (may be NULL when that is 0); contents are overwritten
- *   partition_tokens  16, 32, 64, 128 or 256 (0 = default).  Results do not
- *                 depend on block_size or on where blocks sit in the pool: the
- *                 reduction order is fixed by logical token positions.
+ *   partition_tokens  16, 32, 64, 128, 256, 512 or 1024 (0 = default); 512 and
+ *                 1024 only with the matrix-core grid kernel (PA_KERNEL_MFMA, or
+ *                 AUTO with a bf16 / e4m3 pool), which splits such a partition
+ *                 among 2 or 4 waves per KV head and combines their pieces on chip,
+ *                 so fewer pieces reach the workspace.  Results do not depend on
+ *                 block_size or on where blocks sit in the pool: the reduction
+ *                 order is fixed by logical token positions.
  *   kernel        pa_kernel
  * Outputs are bf16-rounded (nearest even) for bf16 q.  The matrix-core path
  * rounds the softmax probabilities to bf16 before P.V (and sums the same

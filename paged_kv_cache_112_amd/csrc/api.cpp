@@ -14,6 +14,9 @@ namespace {
 constexpr int32_t kDefaultPartition = 256;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr size_t kAlign = 256;
+#ifndef PA_MAX_WG_WAVES
+#define PA_MAX_WG_WAVES 4
+#endif
 #ifndef PA_MAX_HEADS_PER_WG
 #define PA_MAX_HEADS_PER_WG 4
 #endif
@@ -30,7 +33,9 @@ int32_t log2i(int64_t x) {
 
 int32_t elem_bytes(int32_t fmt) { return fmt == PA_F32 ? 4 : fmt == PA_BF16 ? 2 : 1; }
 
-bool valid_partition(int32_t p) { return p == 16 || p == 32 || p == 64 || p == 128 || p == 256; }
+bool valid_partition(int32_t p) {
+  return p == 16 || p == 32 || p == 64 || p == 128 || p == 256 || p == 512 || p == 1024;
+}
 
 struct Workspace {
   size_t m_off, l_off, o_off, bytes;
@@ -100,6 +105,8 @@ pa_status prepare_decode(const void* q, int32_t q_dtype, int32_t num_seqs, int32
   if (k == PA_KERNEL_MFMA_PERSIST && num_seqs > pa::kPersistMaxSeqs) k = PA_KERNEL_MFMA;
   if ((k == PA_KERNEL_MFMA || k == PA_KERNEL_MFMA_PERSIST) && (f32_pair || group > 16)) return PA_ERR_UNSUPPORTED;
   if (k == PA_KERNEL_VALU && group > 8) return PA_ERR_UNSUPPORTED;
+  // partitions beyond 256 tokens: matrix-core grid kernel only (several waves per KV head)
+  if (P > 256 && k != PA_KERNEL_MFMA) return PA_ERR_UNSUPPORTED;
   Workspace ws;
   if (!workspace_layout(num_seqs, num_q_heads, cache->head_dim, max_context_len, P, &ws)) return PA_ERR_SHAPE;
   if (ws.bytes > 0 && (!workspace || workspace_bytes < ws.bytes)) return PA_ERR_WORKSPACE;
@@ -128,9 +135,13 @@ pa_status prepare_decode(const void* q, int32_t q_dtype, int32_t num_seqs, int32
   a.bt_stride = max_blocks_per_seq;
   a.max_parts = ws.parts;
   a.partition_tokens = P;
+  a.waves_per_head = P > 256 ? P / 256 : 1;
   a.heads_per_wg = 1;
   for (int32_t h = PA_MAX_HEADS_PER_WG; h > 1; h /= 2)
-    if (cache->num_kv_heads % h == 0 && (k == PA_KERNEL_MFMA || h <= 4)) { a.heads_per_wg = h; break; }
+    if (cache->num_kv_heads % h == 0 && (k == PA_KERNEL_MFMA || h <= 4) && h * a.waves_per_head <= PA_MAX_WG_WAVES) {
+      a.heads_per_wg = h;
+      break;
+    }
   a.head_groups = cache->num_kv_heads / a.heads_per_wg;
   a.q_fmt = q_dtype;
   a.kv_fmt = cache->dtype;

@@ -11,25 +11,27 @@
 // partitions whose pieces a second kernel merges (LLM stack book, "Performance
 // considerations", split-K over the sequence).
 //
-// How, on gfx950: one wave per (sequence, KV head, partition); a workgroup holds
-// up to four waves (four KV heads) of the same sequence and partition and
-// stages that partition's block-table entries in LDS once.  A tile is 16
-// logical tokens.
+// How, on gfx950: a partition of P tokens belongs to W waves per KV head (W = 1 up
+// to 256 tokens, P / 256 beyond), each taking every W-th 16-token tile; a
+// workgroup holds up to four waves (KV heads x W) of one sequence and partition.
+// With blocks of 16 tokens or more every tile lies in one block, whose id is a
+// uniform scalar load; smaller blocks stage the partition's table entries in LDS.
 //   * q.K^T: v_mfma_f32_16x16x32_bf16 with A = the K tile (row m = token) and
-//     B = q^T (column n = query head of the group).  Lane (m, k-group) of A is
+//     B = q^T (column n = a query head of the group).  Lane (m, k-group) of A is
 //     exactly a 16-byte slice of one K row, so K goes from HBM to the matrix
 //     core with no shuffles.  The sum over d may visit d in any order as long as
 //     q is read in the same order; the e4m3 path uses that freedom to load 16
 //     contiguous bytes per lane.
-//   * The result leaves lane (g, k-group) holding the logits of query head g for
+//   * The result leaves lane (column, k-group) holding that head's logits for
 //     tokens 4*k-group .. +3, which is exactly the A-operand layout of
 //     v_mfma_f32_16x16x16_bf16 for P.V with k = token, so the probabilities feed
 //     the second product in place.  V rows arrive as 16-byte row slices and are
 //     re-paired (v_perm_b32) into token-major B operands.
-//   * Softmax is two-pass within the partition: all logits first (kept in
-//     registers), then one max and one sum, then P.V.  Reduction order depends
-//     only on logical token positions, so results are bitwise identical under
-//     any block size or physical placement.
+//   * Softmax is two-pass within a wave's tiles: all logits first (kept in
+//     registers), then one max and one sum, then P.V.  The W waves of a head are
+//     combined through LDS.  Reduction order depends only on logical token
+//     positions, so results are bitwise identical under any block size or
+//     physical placement.
 // Tokens past the context are clamped to the last valid row for addressing (no
 // stray or out-of-range reads, never a table entry past the context) and given
 // probability 0.
@@ -42,11 +44,14 @@
 #ifndef PA_NT_LOADS
 #define PA_NT_LOADS 0     // 1: K/V tiles loaded with the non-temporal hint (read-once data)
 #endif
+#ifndef PA_MAX_WAVES_PER_EU
+#define PA_MAX_WAVES_PER_EU 8
+#endif
 #ifndef PA_MIN_WAVES_PER_EU
 #define PA_MIN_WAVES_PER_EU 1
 #endif
 #ifndef PA_WG_THREADS
-#define PA_WG_THREADS 256
+#define PA_WG_THREADS 512
 #endif
 
 namespace pa {
@@ -62,15 +67,20 @@ __device__ __forceinline__ int32_t load_uniform(const int32_t* p) {
 __device__ __forceinline__ int head_of_column(int n) { return 4 * (n & 3) + (n >> 2); }
 
 template <bool FP8, int D, int PT, bool BIGBS>
-__global__ __launch_bounds__(PA_WG_THREADS) __attribute__((amdgpu_waves_per_eu(PA_MIN_WAVES_PER_EU, 8)))
+__global__ __launch_bounds__(PA_WG_THREADS) __attribute__((amdgpu_waves_per_eu(PA_MIN_WAVES_PER_EU, PA_MAX_WAVES_PER_EU)))
 void decode_mfma_kernel(const DecodeArgs a) {
-  constexpr int P = 16 * PT;
+  // A partition of P = 16 * PT * W tokens is shared by W waves per KV head: wave w
+  // takes tiles w, w + W, w + 2W, ... (PT of them), and the W partial softmax pieces
+  // are combined through LDS before anything is written.
+  const int W = a.waves_per_head;
+  const int P = 16 * PT * W;
   constexpr int ESZ = FP8 ? 1 : 2;
   constexpr int VEC = D / 16;
   constexpr int NKK = D / 32;
   constexpr int DEPTH = PA_MFMA_DEPTH;
   constexpr int KD = PT < DEPTH ? PT : DEPTH;
-  __shared__ int32_t tbl[BIGBS ? 1 : P];
+  __shared__ int32_t tbl[BIGBS ? 1 : kMaxPartitionTokens];
+  extern __shared__ float xs[];     // combine area, W > 1 only
 
   const int hg = blockIdx.x % a.head_groups;
   int b, part, ctx;
@@ -86,9 +96,11 @@ void decode_mfma_kernel(const DecodeArgs a) {
   }
   const int t0 = part * P;          // same for the whole workgroup
 
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
-  const int kvh = hg * a.heads_per_wg + wave;
+  const int hl = wave % a.heads_per_wg;     // KV head within the workgroup
+  const int w = wave / a.heads_per_wg;      // this wave's share of the partition
+  const int kvh = hg * a.heads_per_wg + hl;
   const int G = a.group;
   const int hq0 = kvh * G;
   const int n = lane & 15;
@@ -124,7 +136,7 @@ void decode_mfma_kernel(const DecodeArgs a) {
   int32_t tile_blk[BIGBS ? PT : 1];
   if constexpr (BIGBS) {
 #pragma unroll
-    for (int i = 0; i < PT; ++i) tile_blk[i] = load_uniform(bt_row + ((min(t0 + 16 * i, ctx - 1) >> log2bs) - lb0));
+    for (int i = 0; i < PT; ++i) tile_blk[i] = load_uniform(bt_row + ((min(t0 + 16 * (i * W + w), ctx - 1) >> log2bs) - lb0));
   }
   auto tile_block = [&](int i) -> int64_t { return (int64_t)tile_blk[i] * block_bytes; };
   auto row_off = [&](int t) -> int64_t {
@@ -147,9 +159,10 @@ void decode_mfma_kernel(const DecodeArgs a) {
     }
   }
 
+  // Wave w of a KV head takes the partition's tiles w, w + W, w + 2W, ... (PT of them).
   auto load_k = [&](int i) {
     KTile<FP8, D> t;
-    const int tok = t0 + 16 * i + n;
+    const int tok = t0 + 16 * (i * W + w) + n;
     const uint8_t* p;
     if constexpr (BIGBS) p = kbase + tile_block(i) + lane_row(tok) + 16 * q4;
     else p = kbase + row_off(tok) + 16 * q4;
@@ -166,7 +179,7 @@ void decode_mfma_kernel(const DecodeArgs a) {
     if constexpr (BIGBS) tb = tile_block(i);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int tok = t0 + 16 * i + 4 * q4 + j;
+      const int tok = t0 + 16 * (i * W + w) + 4 * q4 + j;
       const uint8_t* p;
       if constexpr (BIGBS) p = vbase + tb + lane_row(tok) + n * VEC * ESZ;
       else p = vbase + row_off(tok) + n * VEC * ESZ;
@@ -192,7 +205,7 @@ void decode_mfma_kernel(const DecodeArgs a) {
     const f32x4 s = qk_tile<FP8, D>(cur, qB);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int tok = t0 + 16 * i + 4 * q4 + r;
+      const int tok = t0 + 16 * (i * W + w) + 4 * q4 + r;
       S[i][r] = tok < ctx ? s[r] * a.qk_scale : -INFINITY;
     }
   }
@@ -205,6 +218,8 @@ void decode_mfma_kernel(const DecodeArgs a) {
     for (int r = 0; r < 4; ++r) mx = fmaxf(mx, S[i][r]);
   mx = fmaxf(mx, __shfl_xor(mx, 16));
   mx = fmaxf(mx, __shfl_xor(mx, 32));
+  // a wave whose tiles all lie past the context (W > 1) has no valid token
+  const float mref = mx == -INFINITY ? 0.f : mx;
   uint32_t Pk[PT][2];
   float lsum = 0.f;
 #pragma unroll
@@ -213,7 +228,7 @@ void decode_mfma_kernel(const DecodeArgs a) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       // probabilities enter P.V as bf16; the denominator sums the same rounded values
-      p[r] = (float)(__bf16)__builtin_amdgcn_exp2f(S[i][r] - mx);
+      p[r] = (float)(__bf16)__builtin_amdgcn_exp2f(S[i][r] - mref);
       lsum += p[r];
     }
     Pk[i][0] = pack_bf16(p[0], p[1]);
@@ -233,23 +248,86 @@ void decode_mfma_kernel(const DecodeArgs a) {
     pv_tile<FP8, D>(cur, Pk[i][0], Pk[i][1], O);
   }
 
+  // ---- combine the W waves of each KV head (W > 1) --------------------------------
+  // Per column n (query head head_of_column(n)): M = max_w m_w, L = sum_w 2^(m_w - M) l_w,
+  // and O = sum_w 2^(m_w - M) O_w.  Lane (n, q4) register r of O holds head 4r + q4,
+  // whose column is 4 * q4 + r.  lg[r] is that head's L; (Mn, Ln) are column n's.
+  const int R = (G + 3) >> 2;                  // registers r in use
+  float lg[4], Mn = mx, Ln = lsum;
+  if (W == 1) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) lg[r] = __shfl(lsum, 4 * q4 + r);
+  } else {
+    // this head's area: (m, l) of every wave, then the O registers of waves 1 .. W-1
+    float* base = xs + (int64_t)hl * combine_floats(W);
+    auto ml = [&](int v) { return base + 32 * v; };
+    auto oslot = [&](int v) { return base + 32 * W + (v - 1) * kCombineO; };
+    if (w > 0) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        if (r >= R) break;
+        float* x = oslot(w) + (r * kWave + lane) * VEC;
+#pragma unroll
+        for (int e = 0; e < VEC; e += 4) *reinterpret_cast<f32x4*>(x + e) = f32x4{O[e][r], O[e + 1][r], O[e + 2][r], O[e + 3][r]};
+      }
+    }
+    if (q4 == 0) {
+      ml(w)[n] = mx;
+      ml(w)[16 + n] = lsum;
+    }
+    __syncthreads();
+    if (w > 0) return;
+    auto col_stats = [&](int c, float& Mc, float& Lc, float* aw) {
+      Mc = -INFINITY;
+      for (int v = 0; v < W; ++v) Mc = fmaxf(Mc, ml(v)[c]);
+      Lc = 0.f;
+      for (int v = 0; v < W; ++v) {
+        const float m = ml(v)[c];
+        const float f = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - Mc);
+        if (aw) aw[v] = f;
+        Lc += f * ml(v)[16 + c];
+      }
+    };
+    col_stats(n, Mn, Ln, nullptr);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      lg[r] = 1.f;
+      if (r >= R) continue;
+      float aw[kMaxWavesPerHead];
+      float Mc;
+      col_stats(4 * q4 + r, Mc, lg[r], aw);
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) O[e][r] *= aw[0];
+      for (int v = 1; v < W; ++v) {
+        const float* x = oslot(v) + (r * kWave + lane) * VEC;
+#pragma unroll
+        for (int e = 0; e < VEC; e += 4) {
+          const f32x4 y = *reinterpret_cast<const f32x4*>(x + e);
+          O[e][r] += aw[v] * y[0];
+          O[e + 1][r] += aw[v] * y[1];
+          O[e + 2][r] += aw[v] * y[2];
+          O[e + 3][r] += aw[v] * y[3];
+        }
+      }
+    }
+  }
+
   // ---- write: lane (n, q4) register r holds O[head 4*r + q4][d = VEC*n + e] ----------
   const bool single = ctx <= P;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
-    if (4 * r >= G) break;
+    if (r >= R) break;
     const int g = 4 * r + q4;
-    const float lg = __shfl(lsum, 4 * q4 + r);           // column of head g
     if (g < G) {
       const int64_t hrow = (int64_t)b * a.num_q_heads + hq0 + g;
       if (single) {
-        const float inv = a.v_scale / lg;
-        uint32_t w[VEC / 2];
+        const float inv = a.v_scale / lg[r];
+        uint32_t wv[VEC / 2];
 #pragma unroll
-        for (int c = 0; c < VEC / 2; ++c) w[c] = pack_bf16(O[2 * c][r] * inv, O[2 * c + 1][r] * inv);
+        for (int c = 0; c < VEC / 2; ++c) wv[c] = pack_bf16(O[2 * c][r] * inv, O[2 * c + 1][r] * inv);
         uint16_t* o = out + hrow * D + n * VEC;
-        if constexpr (VEC == 8) st16(o, u32x4{w[0], w[1], w[2], w[3]});
-        else st8(o, u32x2{w[0], w[1]});
+        if constexpr (VEC == 8) st16(o, u32x4{wv[0], wv[1], wv[2], wv[3]});
+        else st8(o, u32x2{wv[0], wv[1]});
       } else {
         float* o = a.ws_o + (hrow * a.max_parts + part) * D + n * VEC;
         if constexpr (VEC == 8) {
@@ -263,19 +341,20 @@ void decode_mfma_kernel(const DecodeArgs a) {
   }
   if (!single && q4 == 0 && head_of_column(n) < G) {
     const int64_t idx = ((int64_t)b * a.num_q_heads + hq0 + head_of_column(n)) * a.max_parts + part;
-    a.ws_m[idx] = mx;
-    a.ws_l[idx] = lsum;
+    a.ws_m[idx] = Mn;
+    a.ws_l[idx] = Ln;
   }
 }
 
 template <bool FP8, int D, bool BIGBS>
 static hipError_t launch_pt(const DecodeArgs& a, dim3 grid, dim3 block, hipStream_t s) {
-  switch (a.partition_tokens) {
-    case 16: hipLaunchKernelGGL((decode_mfma_kernel<FP8, D, 1, BIGBS>), grid, block, 0, s, a); break;
-    case 32: hipLaunchKernelGGL((decode_mfma_kernel<FP8, D, 2, BIGBS>), grid, block, 0, s, a); break;
-    case 64: hipLaunchKernelGGL((decode_mfma_kernel<FP8, D, 4, BIGBS>), grid, block, 0, s, a); break;
-    case 128: hipLaunchKernelGGL((decode_mfma_kernel<FP8, D, 8, BIGBS>), grid, block, 0, s, a); break;
-    case 256: hipLaunchKernelGGL((decode_mfma_kernel<FP8, D, 16, BIGBS>), grid, block, 0, s, a); break;
+  const size_t lds = a.waves_per_head > 1 ? sizeof(float) * combine_floats(a.waves_per_head) * a.heads_per_wg : 0;
+  switch (a.partition_tokens / a.waves_per_head) {
+    case 16: hipLaunchKernelGGL((decode_mfma_kernel<FP8, D, 1, BIGBS>), grid, block, lds, s, a); break;
+    case 32: hipLaunchKernelGGL((decode_mfma_kernel<FP8, D, 2, BIGBS>), grid, block, lds, s, a); break;
+    case 64: hipLaunchKernelGGL((decode_mfma_kernel<FP8, D, 4, BIGBS>), grid, block, lds, s, a); break;
+    case 128: hipLaunchKernelGGL((decode_mfma_kernel<FP8, D, 8, BIGBS>), grid, block, lds, s, a); break;
+    case 256: hipLaunchKernelGGL((decode_mfma_kernel<FP8, D, 16, BIGBS>), grid, block, lds, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -289,7 +368,7 @@ static hipError_t launch_bs(const DecodeArgs& a, dim3 grid, dim3 block, hipStrea
 hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t s) {
   const dim3 grid = a.dense ? dim3((unsigned)(a.max_parts * a.head_groups * a.num_seqs), 1u)
                            : dim3((unsigned)(a.max_parts * a.head_groups), (unsigned)a.num_seqs);
-  const dim3 block((unsigned)(kWave * a.heads_per_wg));
+  const dim3 block((unsigned)(kWave * a.heads_per_wg * a.waves_per_head));
   const bool fp8 = a.kv_fmt == kE4m3;
   if (a.head_dim == 128) return fp8 ? launch_bs<true, 128>(a, grid, block, s) : launch_bs<false, 128>(a, grid, block, s);
   return fp8 ? launch_bs<true, 64>(a, grid, block, s) : launch_bs<false, 64>(a, grid, block, s);

@@ -40,7 +40,15 @@ struct DecodeArgs {
   float qk_scale;            // scale * log2(e) * k_scale
   float v_scale;
   int32_t dense;             // 1: workgroup ids number only existing (sequence, partition) pairs
+  int32_t waves_per_head;    // matrix-core path: waves sharing one KV head's partition (1, 2 or 4)
 };
+
+// Partitions longer than 256 tokens are split among several waves of one workgroup
+// (matrix-core path), whose pieces are combined through LDS.
+constexpr int kMaxPartitionTokens = 1024;
+constexpr int kMaxWavesPerHead = 4;
+constexpr int kCombineO = 4 * 64 * 8;   // floats of one wave's O registers (4 rows r, 64 lanes, up to 8 columns)
+__host__ __device__ constexpr int combine_floats(int waves) { return 32 * waves + (waves - 1) * kCombineO; }
 
 // Largest batch the persistent kernel takes (its per-workgroup running total lives in LDS).
 constexpr int kPersistMaxSeqs = 1024;

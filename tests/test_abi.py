@@ -45,6 +45,8 @@ def test_workspace_bytes():
     assert pa.pa_decode_workspace_bytes(64, 32, 128, 3360, 0) == 2 * al(rows * 4) + al(rows * 128 * 4)
     assert pa.pa_decode_workspace_bytes(4, 4, 64, 200, 16) == 2 * al(4 * 4 * 13 * 4) + al(4 * 4 * 13 * 64 * 4)
     assert pa.pa_decode_workspace_bytes(4, 4, 64, 200, 17) == 0        # invalid partition size
+    assert pa.pa_decode_workspace_bytes(64, 32, 128, 3360, 1024) == 2 * al(64 * 32 * 4 * 4) + al(64 * 32 * 4 * 128 * 4)
+    assert pa.pa_decode_workspace_bytes(64, 32, 128, 3360, 2048) == 0   # beyond the largest partition
     assert pa.pa_decode_workspace_bytes(-1, 4, 64, 200, 0) == 0
 
 
@@ -76,6 +78,8 @@ def _decode(**kw):
     (dict(cache=_cache(block_size=24)), pa.PA_ERR_UNSUPPORTED),
     (dict(cache=_cache(dtype=7)), pa.PA_ERR_DTYPE),
     (dict(partition_tokens=100), pa.PA_ERR_UNSUPPORTED),
+    (dict(partition_tokens=2048), pa.PA_ERR_UNSUPPORTED),
+    (dict(partition_tokens=512), pa.PA_ERR_UNSUPPORTED),                 # f32: vector path, <= 256 only
     (dict(kernel=pa.PA_KERNEL_MFMA), pa.PA_ERR_UNSUPPORTED),            # f32 has no matrix-core path
     (dict(kernel=9), pa.PA_ERR_UNSUPPORTED),
     (dict(kernel=pa.PA_KERNEL_MFMA_PERSIST), pa.PA_ERR_UNSUPPORTED),

@@ -41,7 +41,7 @@ def test_llama3_b64_vector_path_agrees(llama3_b64):
     assert np.abs(a - b).max() <= 2e-2
 
 
-@pytest.mark.parametrize("P", [64, 128])
+@pytest.mark.parametrize("P", [64, 128, 512, 1024])
 def test_llama3_b64_other_partitions(llama3_b64, P):
     _parity(llama3_b64, 2e-2, partition_tokens=P)
 

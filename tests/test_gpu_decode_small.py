@@ -74,6 +74,34 @@ def test_block_sizes(bs, kv, kernel):
     _check(DeviceInputs(build_host_inputs(w)), w, partition_tokens=64, kernel=KERNELS[kernel])
 
 
+# partitions of 512 and 1024 tokens: 2 or 4 waves per KV head, combined on chip
+LONG_EDGE_CTX = EDGE_CTX + [767, 768, 769, 1023, 1024, 1025, 2047, 2048, 2049, 3000]
+
+
+@pytest.mark.parametrize("kv", ["bf16", "e4m3"])
+@pytest.mark.parametrize("hq,hkv,d", [(32, 8, 128), (8, 8, 64), (16, 2, 128), (32, 2, 128)])
+@pytest.mark.parametrize("P", [512, 1024])
+def test_multi_wave_partitions(kv, hq, hkv, d, P):
+    w = custom_workload(LONG_EDGE_CTX, hq, hkv, d, 16, kv, "bf16", seed=hq + d + P + 7)
+    _check(DeviceInputs(build_host_inputs(w)), w, partition_tokens=P, kernel=2)
+
+
+@pytest.mark.parametrize("bs", [1, 4, 64, 256])
+@pytest.mark.parametrize("P", [512, 1024])
+def test_multi_wave_partitions_block_sizes(bs, P):
+    w = custom_workload([1500, 1, 700, 1025], 8, 2, 128, bs, "bf16", "bf16", seed=bs + P)
+    _check(DeviceInputs(build_host_inputs(w)), w, partition_tokens=P, kernel=2)
+
+
+def test_multi_wave_partitions_bitwise_invariant_under_block_size():
+    """The wave that takes a tile is fixed by its logical position: identical bits for any block size."""
+    outs = []
+    for bs in (1, 16, 256):
+        w = custom_workload([2500, 77, 1024], 8, 2, 128, bs, "bf16", "bf16", seed=5)
+        outs.append(from_dev(DeviceInputs(build_host_inputs(w)).decode(partition_tokens=1024, kernel=2)))
+    assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[0], outs[2])
+
+
 def test_gqa_group_16_matrix_core():
     w = custom_workload([70, 333], 32, 2, 128, 16, "bf16", "bf16", seed=3)
     _check(DeviceInputs(build_host_inputs(w)), w, kernel=2)
@@ -183,14 +211,15 @@ def test_large_batch_falls_back_to_grid_kernel():
 # ---------------------------------------------------------------------------
 # the two stages on their own
 # ---------------------------------------------------------------------------
-@pytest.mark.parametrize("kv,kernel", [("bf16", 2), ("f32", 1), ("e4m3", 2)])
-def test_partition_pieces_match_oracle(kv, kernel):
+@pytest.mark.parametrize("kv,kernel,P", [("bf16", 2, 64), ("f32", 1, 64), ("e4m3", 2, 64), ("bf16", 2, 512),
+                                         ("e4m3", 2, 1024)])
+def test_partition_pieces_match_oracle(kv, kernel, P):
     import torch
     import paged_kv_cache_112_amd as pa
-    w = custom_workload([300, 47, 1000, 65], 8, 2, 128, 16, kv, "f32" if kv == "f32" else "bf16", seed=31)
+    ctx = [300, 47, 1000, 65] if P < 512 else [3000, 47, 2100, 1025]
+    w = custom_workload(ctx, 8, 2, 128, 16, kv, "f32" if kv == "f32" else "bf16", seed=31)
     h = build_host_inputs(w)
     dev = DeviceInputs(h)
-    P = 64
     out, ws = pa.decode_partition(dev.q, dev.kc, dev.vc, dev.bt, dev.ctx, w.scale, max_context_len=dev.max_ctx,
                                   partition_tokens=P, kernel=kernel, k_scale=h.k_scale, v_scale=h.v_scale)
     torch.cuda.synchronize()
