@@ -108,8 +108,9 @@ int32_t pa_default_partition_tokens(void);
 /* Workspace bytes pa_decode / pa_decode_partition / pa_merge need for this shape
  * (0 when max_context_len fits in one partition).  partition_tokens = 0 means the
  * default.  Layout, each region aligned to 256 bytes:
- *   m [num_seqs, num_q_heads, J] f32, l [num_seqs, num_q_heads, J] f32,
- *   o [num_seqs, num_q_heads, J, head_dim] f32,  J = ceil(max_context_len / P).
+ *   m [num_seqs, J, num_q_heads] f32, l [num_seqs, J, num_q_heads] f32,
+ *   o [num_seqs, J, num_q_heads, head_dim] f32,  J = ceil(max_context_len / P)
+ * (partition-major: the heads of one partition are contiguous).
  * Calls that share a workspace must be ordered on one stream (they race otherwise).
  * Returns 0 for invalid arguments. */
 size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,

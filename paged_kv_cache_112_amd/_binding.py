@@ -234,15 +234,20 @@ def merge(workspace, context_lens, out, max_context_len, partition_tokens=0, str
 
 
 def workspace_views(workspace, num_seqs, num_q_heads, head_dim, max_context_len, partition_tokens=0):
-    """(m, l, o) float32 views of a workspace, following the layout in include/pa.h."""
+    """(m, l, o) float32 views of a workspace, indexed [seq, head, partition(, column)].
+
+    The storage is partition-major (m, l [B, J, H], o [B, J, H, D], as include/pa.h
+    states); the views are permuted so that callers index by sequence and head first.
+    """
     P = partition_tokens or pa_default_partition_tokens()
     J = 1 if max_context_len <= P else -(-max_context_len // P)
     rows = num_seqs * num_q_heads * J
     al = lambda x: (x + 255) // 256 * 256
     f = workspace.view(_torch().uint8)
-    m = f[0:rows * 4].view(_torch().float32).view(num_seqs, num_q_heads, J)
+    m = f[0:rows * 4].view(_torch().float32).view(num_seqs, J, num_q_heads).permute(0, 2, 1)
     l_off = al(rows * 4)
-    l = f[l_off:l_off + rows * 4].view(_torch().float32).view(num_seqs, num_q_heads, J)
+    l = f[l_off:l_off + rows * 4].view(_torch().float32).view(num_seqs, J, num_q_heads).permute(0, 2, 1)
     o_off = l_off + al(rows * 4)
-    o = f[o_off:o_off + rows * head_dim * 4].view(_torch().float32).view(num_seqs, num_q_heads, J, head_dim)
+    o = (f[o_off:o_off + rows * head_dim * 4].view(_torch().float32).view(num_seqs, J, num_q_heads, head_dim)
+         .permute(0, 2, 1, 3))
     return m, l, o

@@ -42,7 +42,8 @@
 #define PA_MFMA_DEPTH 3   // K or V tiles in flight per wave
 #endif
 #ifndef PA_NT_LOADS
-#define PA_NT_LOADS 0     // 1: K/V tiles loaded with the non-temporal hint (read-once data)
+#define PA_NT_LOADS 1     // K/V tiles are read once: loaded with the non-temporal hint, so they do not
+                          // push the partition pieces (written back later) out of the L2
 #endif
 #ifndef PA_MAX_WAVES_PER_EU
 #define PA_MAX_WAVES_PER_EU 8
@@ -329,7 +330,7 @@ void decode_mfma_kernel(const DecodeArgs a) {
         if constexpr (VEC == 8) st16(o, u32x4{wv[0], wv[1], wv[2], wv[3]});
         else st8(o, u32x2{wv[0], wv[1]});
       } else {
-        float* o = a.ws_o + (hrow * a.max_parts + part) * D + n * VEC;
+        float* o = a.ws_o + piece_row(b, part, hq0 + g, a.max_parts, a.num_q_heads) * D + n * VEC;
         if constexpr (VEC == 8) {
           st16(o, __builtin_bit_cast(u32x4, f32x4{O[0][r], O[1][r], O[2][r], O[3][r]} * a.v_scale));
           st16(o + 4, __builtin_bit_cast(u32x4, f32x4{O[4][r], O[5][r], O[6][r], O[7][r]} * a.v_scale));
@@ -340,7 +341,7 @@ void decode_mfma_kernel(const DecodeArgs a) {
     }
   }
   if (!single && q4 == 0 && head_of_column(n) < G) {
-    const int64_t idx = ((int64_t)b * a.num_q_heads + hq0 + head_of_column(n)) * a.max_parts + part;
+    const int64_t idx = piece_row(b, part, hq0 + head_of_column(n), a.max_parts, a.num_q_heads);
     a.ws_m[idx] = Mn;
     a.ws_l[idx] = Ln;
   }

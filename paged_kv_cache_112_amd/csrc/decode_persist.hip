@@ -209,7 +209,7 @@ __global__ __launch_bounds__(256) void decode_persist_kernel(const DecodeArgs a)
           if constexpr (VEC == 8) st16(o, u32x4{w[0], w[1], w[2], w[3]});
           else st8(o, u32x2{w[0], w[1]});
         } else {
-          float* o = a.ws_o + (hrow * a.max_parts + r.part) * D + n * VEC;
+          float* o = a.ws_o + piece_row(r.b, r.part, hq0 + g, a.max_parts, a.num_q_heads) * D + n * VEC;
           st16(o, __builtin_bit_cast(u32x4, f32x4{O[0][rr], O[1][rr], O[2][rr], O[3][rr]} * a.v_scale));
           if constexpr (VEC == 8)
             st16(o + 4, __builtin_bit_cast(u32x4, f32x4{O[4][rr], O[5][rr], O[6][rr], O[7][rr]} * a.v_scale));
@@ -217,7 +217,7 @@ __global__ __launch_bounds__(256) void decode_persist_kernel(const DecodeArgs a)
       }
     }
     if (!single && q4 == 0 && n < G) {
-      const int64_t idx = ((int64_t)r.b * a.num_q_heads + hq0 + n) * a.max_parts + r.part;
+      const int64_t idx = piece_row(r.b, r.part, hq0 + n, a.max_parts, a.num_q_heads);
       a.ws_m[idx] = mx;
       a.ws_l[idx] = lsum;
     }

@@ -197,12 +197,13 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(const DecodeArgs a) {
           else static_cast<uint16_t*>(a.out)[hrow * D + d0 + e] = __builtin_bit_cast(uint16_t, (__bf16)y);
         }
       } else {
-        float* o = a.ws_o + (hrow * a.max_parts + part) * D + d0;
+        const int64_t prow = piece_row(b, part, hq0 + g, a.max_parts, a.num_q_heads);
+        float* o = a.ws_o + prow * D + d0;
 #pragma unroll
         for (int e = 0; e < E; ++e) o[e] = acc[g][e] * a.v_scale;
         if (cl == 0) {
-          a.ws_m[hrow * a.max_parts + part] = mg[g];
-          a.ws_l[hrow * a.max_parts + part] = lg[g];
+          a.ws_m[prow] = mg[g];
+          a.ws_l[prow] = lg[g];
         }
       }
     }

@@ -53,6 +53,13 @@ __host__ __device__ constexpr int combine_floats(int waves) { return 32 * waves 
 // Largest batch the persistent kernel takes (its per-workgroup running total lives in LDS).
 constexpr int kPersistMaxSeqs = 1024;
 
+// Row of the workspace pieces of (sequence b, partition j, query head h): the
+// pieces are laid out partition-major, m / l [B, J, H] and o [B, J, H, D], so the
+// heads of one partition -- written together by one workgroup -- are contiguous.
+__host__ __device__ inline int64_t piece_row(int b, int j, int h, int max_parts, int num_q_heads) {
+  return ((int64_t)b * max_parts + j) * num_q_heads + h;
+}
+
 struct MergeArgs {
   const float* ws_m;
   const float* ws_l;

@@ -27,16 +27,18 @@ __global__ __launch_bounds__(64) void merge_kernel(const MergeArgs a) {
   const int ctx = a.context_lens[b];
   const int n = (ctx + a.partition_tokens - 1) / a.partition_tokens;
   if (n <= 1) return;
-  const int64_t base = ((int64_t)b * a.num_q_heads + h) * a.max_parts;
-  const float* ms = a.ws_m + base;
-  const float* ls = a.ws_l + base;
-  const float* os = a.ws_o + base * D + d0;
+  // pieces are partition-major: partition j of this (sequence, head) is row piece_row(b, j, h)
+  const int64_t r0 = piece_row(b, 0, h, a.max_parts, a.num_q_heads);
+  const int64_t H = a.num_q_heads;
+  const float* ms = a.ws_m + r0;            // ms[j * H]
+  const float* ls = a.ws_l + r0;
+  const float* os = a.ws_o + r0 * D + d0;   // os[j * H * D]
 
   float M = -INFINITY;
-  for (int j = lane; j < n; j += kWave) M = fmaxf(M, ms[j]);
+  for (int j = lane; j < n; j += kWave) M = fmaxf(M, ms[j * H]);
   M = wave_max(M);
   float L = 0.f;
-  for (int j = lane; j < n; j += kWave) L += ls[j] * __builtin_amdgcn_exp2f(ms[j] - M);
+  for (int j = lane; j < n; j += kWave) L += ls[j * H] * __builtin_amdgcn_exp2f(ms[j * H] - M);
   L = wave_sum(L);
 
   // four partitions per wave load; all loads of a round of 16 partitions are issued together
@@ -50,9 +52,9 @@ __global__ __launch_bounds__(64) void merge_kernel(const MergeArgs a) {
     for (int u = 0; u < 4; ++u) {
       const int j = j0 + 4 * u + pg;
       const int jc = min(j, n - 1);
-      wv[u] = j < n ? __builtin_amdgcn_exp2f(ms[jc] - M) : 0.f;
+      wv[u] = j < n ? __builtin_amdgcn_exp2f(ms[jc * H] - M) : 0.f;
 #pragma unroll
-      for (int c = 0; c < DPL / 4; ++c) ov[u][c] = __builtin_bit_cast(f32x4, ld16(os + (int64_t)jc * D + 4 * c));
+      for (int c = 0; c < DPL / 4; ++c) ov[u][c] = __builtin_bit_cast(f32x4, ld16(os + jc * H * D + 4 * c));
     }
 #pragma unroll
     for (int u = 0; u < 4; ++u)

@@ -132,3 +132,21 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(_binding, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError, match="not built"):
         _binding.lib()
+
+
+def test_workspace_views_are_partition_major():
+    """m, l [B, J, H] and o [B, J, H, D] in storage; the views index [B, H, J(, D)]."""
+    import torch
+    B, H, D, ctx, P = 3, 4, 64, 100, 32
+    J = -(-ctx // P)
+    ws = torch.zeros(pa.pa_decode_workspace_bytes(B, H, D, ctx, P), dtype=torch.uint8)
+    m, l, o = pa.workspace_views(ws, B, H, D, ctx, P)
+    assert m.shape == (B, H, J) and o.shape == (B, H, J, D)
+    m[1, 2, 3] = 7.0
+    o[2, 1, 0, 5] = 9.0
+    raw_m = ws[:B * J * H * 4].view(torch.float32)
+    assert raw_m[(1 * J + 3) * H + 2] == 7.0 and float(raw_m.sum()) == 7.0
+    al = lambda x: (x + 255) // 256 * 256
+    o_off = 2 * al(B * J * H * 4)
+    raw_o = ws[o_off:o_off + B * J * H * D * 4].view(torch.float32)
+    assert raw_o[((2 * J + 0) * H + 1) * D + 5] == 9.0 and float(raw_o.sum()) == 9.0
