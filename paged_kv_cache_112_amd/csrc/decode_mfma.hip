@@ -41,9 +41,16 @@
 #ifndef PA_MFMA_DEPTH
 #define PA_MFMA_DEPTH 3   // K or V tiles in flight per wave
 #endif
-#ifndef PA_NT_LOADS
-#define PA_NT_LOADS 1     // K/V tiles are read once: loaded with the non-temporal hint, so they do not
-                          // push the partition pieces (written back later) out of the L2
+// Cache hints for the read-once K and V streams.  A V load instruction covers whole
+// 128-byte lines (four rows x 256 bytes), so V is loaded non-temporally and does not
+// push the partition pieces (written back later) out of the L2.  A K load
+// instruction covers half of each line of 16 rows; the other half comes with the
+// next instruction, so K keeps the default policy and the line stays for it.
+#ifndef PA_NT_K
+#define PA_NT_K 0
+#endif
+#ifndef PA_NT_V
+#define PA_NT_V 1
 #endif
 #ifndef PA_MAX_WAVES_PER_EU
 #define PA_MAX_WAVES_PER_EU 8
@@ -169,7 +176,7 @@ void decode_mfma_kernel(const DecodeArgs a) {
     else p = kbase + row_off(tok) + 16 * q4;
 #pragma unroll
     for (int j = 0; j < KTile<FP8, D>::N; ++j) {
-      if constexpr (PA_NT_LOADS) t.w[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p + 64 * j));
+      if constexpr (PA_NT_K) t.w[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p + 64 * j));
       else t.w[j] = ld16(p + 64 * j);
     }
     return t;
@@ -184,7 +191,7 @@ void decode_mfma_kernel(const DecodeArgs a) {
       const uint8_t* p;
       if constexpr (BIGBS) p = vbase + tb + lane_row(tok) + n * VEC * ESZ;
       else p = vbase + row_off(tok) + n * VEC * ESZ;
-      if constexpr (PA_NT_LOADS) t.w[j] = __builtin_nontemporal_load(reinterpret_cast<const typename VTile<FP8, D>::W*>(p));
+      if constexpr (PA_NT_V) t.w[j] = __builtin_nontemporal_load(reinterpret_cast<const typename VTile<FP8, D>::W*>(p));
       else t.w[j] = *reinterpret_cast<const typename VTile<FP8, D>::W*>(p);
     }
     return t;
