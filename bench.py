@@ -102,6 +102,80 @@ def cpu_baseline(w):
                       f"one thread, median of {len(times)} runs"}
 
 
+def _time_launches(torch, fn, reps, warmup):
+    """Average microseconds per call of fn() launched back to back, HIP events on the current stream."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    s = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(s)
+    for _ in range(reps):
+        fn()
+    e1.record(s)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / reps
+
+
+def side_op(args, w, torch, pa):
+    """One JSON line for a measurement beside the headline step (not the default bench line)."""
+    dev = torch.device("cuda:0")
+    fp8 = w.kv_dtype == "e4m3"
+    kv_dtype = torch.uint8 if fp8 else torch.bfloat16
+    esz = 1 if fp8 else 2
+    shape = (w.num_blocks, w.block_size, w.num_kv_heads, w.head_dim)
+    block_bytes = w.block_size * w.num_kv_heads * w.head_dim * esz
+    reps, warm = max(args.steps, 10), max(args.warmup, 3)
+    if args.op == "copy_blocks":
+        # LAYERS pool pairs, used in turn, so the 256 MB MALL cannot serve a block copied by
+        # an earlier call
+        pools = [(torch.randint(0, 255, shape, dtype=torch.uint8, device=dev).view(kv_dtype),
+                  torch.randint(0, 255, shape, dtype=torch.uint8, device=dev).view(kv_dtype))
+                 for _ in range(LAYERS)]
+        rng = np.random.default_rng(5)
+        perm = rng.permutation(w.num_blocks).astype(np.int32)
+        half = w.num_blocks // 2
+        lines = []
+        turn = [0]
+
+        def call(src, dst):
+            kc, vc = pools[turn[0] % LAYERS]
+            turn[0] += 1
+            pa.copy_blocks(kc, vc, src, dst)
+
+        # bulk: half the pool copied onto the other half; step-sized: one block per sequence
+        for n in (half, w.num_seqs):
+            src = torch.from_numpy(perm[:n].copy()).to(dev)
+            dst = torch.from_numpy(perm[half:half + n].copy()).to(dev)
+            us = _time_launches(torch, lambda: call(src, dst), reps, warm)
+            nbytes = 2 * 2 * n * block_bytes                  # K and V, read and written
+            gbs = nbytes / us / 1e3
+            lines.append({"pairs": n, "us_per_call": round(us, 2), "bytes": nbytes, "GB/s": round(gbs, 1),
+                          "frac_of_8TBps": round(gbs / HBM_PEAK_GBS, 4)})
+        print(json.dumps({"metric": "pa_copy_blocks (copy-on-write block copies)", "workload": w.name,
+                          "block_bytes": block_bytes, "dtype": w.kv_dtype, "results": lines,
+                          "timing": "HIP events around back-to-back calls"}))
+        return
+    # write_prefill: every context token of the batch through pa_write_kv in one call
+    kc = torch.zeros(shape, dtype=kv_dtype, device=dev)
+    vc = torch.zeros(shape, dtype=kv_dtype, device=dev)
+    slots = np.concatenate([w.slots(b, w.owned_positions(b)) for b in range(w.num_seqs)]).astype(np.int32)
+    n = len(slots)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(w.seed)
+    k = torch.randn((n, w.num_kv_heads, w.head_dim), generator=gen, device=dev).to(torch.bfloat16)
+    v = torch.randn((n, w.num_kv_heads, w.head_dim), generator=gen, device=dev).to(torch.bfloat16)
+    sl = torch.from_numpy(slots).to(dev)
+    ks = float(np.float32(4.8 / 448)) if fp8 else 1.0
+    us = _time_launches(torch, lambda: pa.write_kv(k, v, sl, kc, vc, ks, ks), reps, warm)
+    nbytes = n * w.num_kv_heads * w.head_dim * 2 * (2 + esz) + 4 * n
+    gbs = nbytes / us / 1e3
+    print(json.dumps({"metric": "pa_write_kv, prefill-shaped (every context token in one call)",
+                      "workload": w.name, "tokens": n, "us_per_call": round(us, 2), "bytes": nbytes,
+                      "GB/s": round(gbs, 1), "frac_of_8TBps": round(gbs / HBM_PEAK_GBS, 4),
+                      "timing": "HIP events around back-to-back calls"}))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -115,6 +189,9 @@ def main():
     ap.add_argument("--block-size", type=int, default=None, help="block size for llama2_7b_mha")
     ap.add_argument("--copy-calibrate", type=int, default=0, metavar="MIB",
                     help="only copy MIB MiB with torch (a plain copy of known size, for counter scaling)")
+    ap.add_argument("--op", default="decode", choices=["decode", "copy_blocks", "write_prefill"],
+                    help="decode: the hot-path step (the headline line); copy_blocks: copy-on-write block "
+                         "copies over the workload's pools; write_prefill: pa_write_kv of every context token")
     ap.add_argument("--contiguous", action="store_true",
                     help="identity-ordered block tables (each sequence's blocks adjacent): the contiguous comparator")
     args = ap.parse_args()
@@ -147,6 +224,8 @@ def main():
         from workloads import deal_tables
         w.block_tables, _ = deal_tables(w.context_lens, w.block_size, np.arange(w.num_blocks, dtype=np.int32))
     B, hq, hkv, d, bs = w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim, w.block_size
+    if args.op != "decode":
+        return side_op(args, w, torch, pa)
 
     def to_dev(a):
         a = np.ascontiguousarray(a)

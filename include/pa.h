@@ -102,6 +102,27 @@ pa_status pa_write_kv(const void* k, const void* v, int32_t in_dtype, int32_t nu
                       const int32_t* slot_mapping, void* k_cache, void* v_cache,
                       const pa_kv_cache* cache, void* stream);
 
+/* Block copy for copy-on-write.
+ *
+ * For every pair i < num_pairs, copies physical block src[i] to physical block
+ * dst[i] in both pools: all block_size rows, all KV heads, bytes as stored
+ * (any pool format).  This is the device half of copy-on-write: before a
+ * sequence appends into a block that other sequences still reference, the
+ * allocator hands it a fresh block, the shared block is copied there, and the
+ * sequence's table entry is redirected (LLM stack book, "Copy-on-write for
+ * shared prefixes"; ai-infra-handbooks "Paged KV cache", exercise 2).
+ *
+ *   k_cache, v_cache  device pools, written in place (blocks dst[i] only)
+ *   src, dst      device int32 [num_pairs]; a pair with either id outside
+ *                 [0, num_blocks) (negative padding included) is skipped
+ *   num_pairs     0 .. 65535
+ * Every copy reads the pools as they were before the call: no dst may also
+ * appear as a src, and dst ids must be distinct (undefined otherwise).
+ * Errors: PA_ERR_NULL, PA_ERR_SHAPE, PA_ERR_DTYPE, PA_ERR_UNSUPPORTED,
+ * PA_ERR_HIP.  num_pairs == 0 is a no-op returning PA_OK. */
+pa_status pa_copy_blocks(void* k_cache, void* v_cache, const pa_kv_cache* cache, const int32_t* src,
+                         const int32_t* dst, int32_t num_pairs, void* stream);
+
 /* Partition size (tokens) used when a call passes partition_tokens = 0. */
 int32_t pa_default_partition_tokens(void);
 

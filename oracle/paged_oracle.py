@@ -23,6 +23,8 @@ What is computed (each function names its passage):
   * ``write_kv``: every new token i with slot_mapping[i] >= 0 lands in
     block slot // B at offset slot % B of the flat pool; a same-format write
     is a byte copy, an e4m3 pool stores the quantized value.
+  * ``copy_blocks``: copy-on-write's device step, whole physical blocks of both
+    pools copied as stored.
   * ``decode``: for every sequence and query head, softmax(scale * q . K^T) V
     over the context's tokens, gathering each token's K/V row through the
     block table.  Both the LLM stack book ("The PagedAttention Kernel") and the
@@ -195,6 +197,26 @@ def write_kv(k_cache: np.ndarray, v_cache: np.ndarray, k: np.ndarray, v: np.ndar
         blk, off = divmod(int(s), B)
         k_cache[blk, off] = kq[i]
         v_cache[blk, off] = vq[i]
+
+
+def copy_blocks(k_cache: np.ndarray, v_cache: np.ndarray, src, dst) -> None:
+    """Copy-on-write's device step, in place: physical block src[i] -> dst[i] in both pools.
+
+    LLM stack book, "Copy-on-write for shared prefixes": a sequence about to
+    append into a block whose reference count exceeds one gets a fresh block, the
+    contested block is copied into it, and the sequence's table entry is
+    redirected; ai-infra-handbooks "Paged KV cache", exercise 2, describes the
+    same steps.  A block is copied whole -- every offset, every KV head -- as
+    stored.  Every copy reads the pools as they were before the call; a pair with
+    an id outside the pool (negative padding included) is skipped.
+    """
+    nb = k_cache.shape[0]
+    k_before, v_before = k_cache.copy(), v_cache.copy()
+    for s, d in zip(np.asarray(src, dtype=np.int64), np.asarray(dst, dtype=np.int64)):
+        if not (0 <= s < nb and 0 <= d < nb):
+            continue
+        k_cache[d] = k_before[s]
+        v_cache[d] = v_before[s]
 
 
 # ---------------------------------------------------------------------------

@@ -20,8 +20,8 @@ PA_F32, PA_BF16, PA_FP8_E4M3 = 0, 1, 2
 # pa_kernel
 PA_KERNEL_AUTO, PA_KERNEL_VALU, PA_KERNEL_MFMA, PA_KERNEL_MFMA_PERSIST = 0, 1, 2, 3
 
-EXPORTED = ("pa_write_kv", "pa_decode", "pa_decode_partition", "pa_merge", "pa_decode_workspace_bytes",
-            "pa_default_partition_tokens", "pa_status_str")
+EXPORTED = ("pa_write_kv", "pa_copy_blocks", "pa_decode", "pa_decode_partition", "pa_merge",
+            "pa_decode_workspace_bytes", "pa_default_partition_tokens", "pa_status_str")
 
 
 class PaKvCache(ctypes.Structure):
@@ -53,6 +53,8 @@ def lib() -> ctypes.CDLL:
         L = ctypes.CDLL(LIB_PATH)
         L.pa_write_kv.argtypes = [_vp, _vp, _i32, _i32, _vp, _vp, _vp, ctypes.POINTER(PaKvCache), _vp]
         L.pa_write_kv.restype = ctypes.c_int
+        L.pa_copy_blocks.argtypes = [_vp, _vp, ctypes.POINTER(PaKvCache), _vp, _vp, _i32, _vp]
+        L.pa_copy_blocks.restype = ctypes.c_int
         L.pa_decode.argtypes = _DECODE_ARGS
         L.pa_decode.restype = ctypes.c_int
         L.pa_decode_partition.argtypes = _DECODE_ARGS
@@ -83,6 +85,10 @@ def check(status: int) -> None:
 # ---------------------------------------------------------------------------
 def pa_write_kv(k, v, in_dtype, num_tokens, slot_mapping, k_cache, v_cache, cache: PaKvCache, stream) -> int:
     return lib().pa_write_kv(k, v, in_dtype, num_tokens, slot_mapping, k_cache, v_cache, ctypes.byref(cache), stream)
+
+
+def pa_copy_blocks(k_cache, v_cache, cache: PaKvCache, src, dst, num_pairs, stream) -> int:
+    return lib().pa_copy_blocks(k_cache, v_cache, ctypes.byref(cache), src, dst, num_pairs, stream)
 
 
 def pa_decode(q, q_dtype, num_seqs, num_q_heads, k_cache, v_cache, cache: PaKvCache, block_tables,
@@ -164,6 +170,18 @@ def write_kv(k, v, slot_mapping, k_cache, v_cache, k_scale: float = 1.0, v_scale
     desc = cache_desc(k_cache, k_scale, v_scale)
     check(pa_write_kv(_ptr(k), _ptr(v), dtype_code(k), k.shape[0], _ptr(slot_mapping), _ptr(k_cache),
                       _ptr(v_cache), desc, _stream(stream)))
+
+
+def copy_blocks(k_cache, v_cache, src, dst, stream=None) -> None:
+    """pa_copy_blocks on torch tensors: block src[i] -> block dst[i] in both pools (int32 device ids)."""
+    if k_cache.shape != v_cache.shape or k_cache.dtype != v_cache.dtype:
+        raise ValueError("K and V pools must match")
+    if src.dtype != _torch().int32 or dst.dtype != _torch().int32 or src.numel() != dst.numel():
+        raise ValueError("src and dst must be int32 tensors of equal length")
+    if src.numel() == 0:
+        return
+    desc = cache_desc(k_cache)
+    check(pa_copy_blocks(_ptr(k_cache), _ptr(v_cache), desc, _ptr(src), _ptr(dst), src.numel(), _stream(stream)))
 
 
 def decode_workspace_bytes(num_seqs, num_q_heads, head_dim, max_context_len, partition_tokens=0) -> int:

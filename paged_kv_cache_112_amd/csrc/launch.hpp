@@ -69,7 +69,19 @@ struct MergeArgs {
   int32_t num_seqs, num_q_heads, head_dim, max_parts, partition_tokens, out_fmt;
 };
 
+struct CopyArgs {
+  uint8_t* k_cache;
+  uint8_t* v_cache;
+  const int32_t* src;        // [num_pairs] physical block ids
+  const int32_t* dst;
+  int64_t num_blocks;
+  int64_t block_bytes;       // bs * H_kv * D * elem, a multiple of 16
+  int64_t chunks;            // block_bytes / 16
+  int32_t num_pairs;
+};
+
 hipError_t launch_write_kv(const WriteArgs& a, hipStream_t stream);
+hipError_t launch_copy_blocks(const CopyArgs& a, hipStream_t stream);
 hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_decode_persist(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_decode_valu(const DecodeArgs& a, hipStream_t stream);

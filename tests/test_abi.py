@@ -150,3 +150,21 @@ def test_workspace_views_are_partition_major():
     o_off = 2 * al(B * J * H * 4)
     raw_o = ws[o_off:o_off + B * J * H * D * 4].view(torch.float32)
     assert raw_o[((2 * J + 0) * H + 1) * D + 5] == 9.0 and float(raw_o.sum()) == 9.0
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(k_cache=None), pa.PA_ERR_NULL),
+    (dict(src=None), pa.PA_ERR_NULL),
+    (dict(num_pairs=-1), pa.PA_ERR_SHAPE),
+    (dict(num_pairs=65536), pa.PA_ERR_SHAPE),
+    (dict(cache=_cache(dtype=7)), pa.PA_ERR_DTYPE),
+    (dict(cache=_cache(head_dim=96)), pa.PA_ERR_UNSUPPORTED),
+    (dict(num_pairs=0), pa.PA_OK),                                   # no-op: nothing enqueued
+])
+def test_copy_blocks_checks(kw, status):
+    a = dict(k_cache=FAKE, v_cache=FAKE, cache=_cache(dtype=pa.PA_BF16), src=FAKE, dst=FAKE, num_pairs=3,
+             stream=None)
+    a.update(kw)
+    if a["num_pairs"] != 0 and status == pa.PA_OK:
+        pytest.skip("a valid call would launch")
+    assert pa.pa_copy_blocks(**a) == status
