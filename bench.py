@@ -176,6 +176,46 @@ def side_op(args, w, torch, pa):
                       "timing": "HIP events around back-to-back calls"}))
 
 
+def bench_attention(args, torch, pa):
+    """pa_paged_attention on llama3_8b_chunk512: the last 512-token chunk of 32 sequences."""
+    from workloads import make_mq_config
+    w = make_mq_config("llama3_8b_chunk512")
+    dev = torch.device("cuda:0")
+    shape = (w.num_blocks, w.block_size, w.num_kv_heads, w.head_dim)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(w.seed)
+    pools = [(torch.randn(shape, generator=gen, device=dev).to(torch.bfloat16),
+              torch.randn(shape, generator=gen, device=dev).to(torch.bfloat16)) for _ in range(LAYERS)]
+    qsl = w.query_start_loc()
+    n = int(qsl[-1])
+    q = torch.randn((n, w.num_q_heads, w.head_dim), generator=gen, device=dev).to(torch.bfloat16)
+    out = torch.empty_like(q)
+    bt = torch.from_numpy(w.block_tables).to(dev)
+    sl = torch.from_numpy(w.context_lens).to(dev)
+    qs = torch.from_numpy(qsl).to(dev)
+    maxq = int(w.query_lens.max())
+    turn = [0]
+
+    def call():
+        kc, vc = pools[turn[0] % LAYERS]
+        turn[0] += 1
+        pa.paged_attention(q, kc, vc, bt, sl, qs, w.scale, maxq, out=out)
+
+    us = _time_launches(torch, call, max(args.steps, 10), max(args.warmup, 3))
+    # causal work actually needed: new token j of sequence b sees p + 1 keys, p = S - n + j
+    keys = sum(int(S) * int(nq) - int(nq) * (int(nq) - 1) // 2 for S, nq in zip(w.context_lens, w.query_lens))
+    flops = 4 * w.head_dim * w.num_q_heads * keys
+    kv_bytes = int(w.context_lens.sum()) * w.num_kv_heads * w.head_dim * 2 * 2
+    qo_bytes = 2 * n * w.num_q_heads * w.head_dim * 2
+    tflops = flops / us / 1e6
+    print(json.dumps({"metric": "pa_paged_attention (multi-query, causal), llama3_8b_chunk512",
+                      "workload": w.name, "new_tokens": n, "us_per_call": round(us, 2),
+                      "TFLOP/s": round(tflops, 1), "frac_of_bf16_mfma_2.5PF": round(tflops / 2500.0, 4),
+                      "unique_kv_and_qo_bytes": kv_bytes + qo_bytes,
+                      "GB/s_unique": round((kv_bytes + qo_bytes) / us / 1e3, 1),
+                      "timing": "HIP events around back-to-back calls, 8 pool copies in turn"}))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -189,9 +229,10 @@ def main():
     ap.add_argument("--block-size", type=int, default=None, help="block size for llama2_7b_mha")
     ap.add_argument("--copy-calibrate", type=int, default=0, metavar="MIB",
                     help="only copy MIB MiB with torch (a plain copy of known size, for counter scaling)")
-    ap.add_argument("--op", default="decode", choices=["decode", "copy_blocks", "write_prefill"],
+    ap.add_argument("--op", default="decode", choices=["decode", "copy_blocks", "write_prefill", "attention"],
                     help="decode: the hot-path step (the headline line); copy_blocks: copy-on-write block "
-                         "copies over the workload's pools; write_prefill: pa_write_kv of every context token")
+                         "copies over the workload's pools; write_prefill: pa_write_kv of every context token; "
+                         "attention: multi-query paged attention on llama3_8b_chunk512")
     ap.add_argument("--contiguous", action="store_true",
                     help="identity-ordered block tables (each sequence's blocks adjacent): the contiguous comparator")
     args = ap.parse_args()
@@ -217,6 +258,8 @@ def main():
     if not os.path.exists(pa.LIB_PATH):
         from paged_kv_cache_112_amd.build import build
         build()
+    if args.op == "attention":
+        return bench_attention(args, torch, pa)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     w = make_config(args.workload, args.block_size) if args.workload == "llama2_7b_mha" else make_config(args.workload)

@@ -214,6 +214,38 @@ pa_status pa_merge(const void* workspace, size_t workspace_bytes, int32_t num_se
                    int32_t head_dim, const int32_t* context_lens, int32_t max_context_len,
                    int32_t partition_tokens, int32_t out_dtype, void* out, void* stream);
 
+/* Multi-query paged attention: several new tokens per sequence (chunked prefill,
+ * a full prefill, or decode as the one-token case), causal within each sequence.
+ *
+ * Sequence b's new tokens are rows query_start_loc[b] .. query_start_loc[b+1]-1 of
+ * q; they are the last n_b = query_start_loc[b+1] - query_start_loc[b] positions of
+ * its context of seq_lens[b] tokens (their K/V already written, e.g. by
+ * pa_write_kv).  New token j, at position p = seq_lens[b] - n_b + j, attends to the
+ * positions 0 .. p of its own sequence:
+ *   out[row, h, :] = softmax_t<=p(scale * q[row, h, :] . K[b, t, kvh, :]) V[b, t, kvh, :]
+ * with kvh = h / (num_q_heads / num_kv_heads) and token t read through the block
+ * table as in pa_decode (ai-infra-handbooks "Paged KV cache", section "Paged
+ * attention": block_tables, seq_lens and query_start_loc; the causal mask offset by
+ * seq_len - num_new; the result equals contiguous attention).
+ *
+ *   q, out        device [num_tokens, num_q_heads, head_dim] bf16 (q_dtype PA_BF16)
+ *   cache         a PA_BF16 or PA_FP8_E4M3 pool; num_q_heads / num_kv_heads in
+ *                 {1, 2, 4, 8, 16}
+ *   block_tables  device int32 [num_seqs, max_blocks_per_seq]
+ *   seq_lens      device int32 [num_seqs], context length including the new tokens
+ *   query_start_loc  device int32 [num_seqs + 1], nondecreasing, from 0 to num_tokens
+ *   max_query_len host-known bound on n_b (sizes the grid)
+ * The matrix-core path rounds probabilities to bf16 before P.V, as pa_decode does.
+ * A sequence whose rows fall outside [0, num_tokens) or whose n_b exceeds
+ * seq_lens[b] is skipped (its out rows are left untouched).
+ * Errors: PA_ERR_NULL, PA_ERR_SHAPE, PA_ERR_DTYPE, PA_ERR_UNSUPPORTED, PA_ERR_HIP.
+ * num_tokens == 0 or num_seqs == 0 is a no-op returning PA_OK. */
+pa_status pa_paged_attention(const void* q, int32_t q_dtype, int32_t num_tokens, int32_t num_seqs,
+                             int32_t num_q_heads, const void* k_cache, const void* v_cache,
+                             const pa_kv_cache* cache, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                             const int32_t* seq_lens, const int32_t* query_start_loc, int32_t max_query_len,
+                             float scale, void* out, void* stream);
+
 /* Static, human-readable name of a status code. */
 const char* pa_status_str(pa_status status);
 

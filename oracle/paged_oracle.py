@@ -32,6 +32,8 @@ What is computed (each function names its passage):
     Overview") state that the paged kernel computes exactly the values of plain
     attention, so the oracle computes the plain definition: gather the tokens in
     logical order, two-pass softmax, weighted sum.
+  * ``paged_attention``: several new tokens per sequence, each attending causally
+    to the context up to its own position (ai-infra-handbooks "Paged attention").
   * ``decode_partials`` / ``merge_partials``: the split-K decomposition of the
     same sum over token partitions (LLM stack book, "Performance
     considerations": long sequences are split across thread blocks and the
@@ -273,6 +275,44 @@ def decode(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray, block_tables
                 logits = s64 * (K @ qf[b, h])
                 w = np.exp(logits - logits.max())
                 out[b, h] = (w @ V) / w.sum()
+    return out
+
+
+def paged_attention(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray, block_tables: np.ndarray,
+                    seq_lens: np.ndarray, query_start_loc: np.ndarray, scale: float, kv_format: str,
+                    q_format: str, k_scale: float = 1.0, v_scale: float = 1.0, rows=None) -> np.ndarray:
+    """Causal attention of several new tokens per sequence over the paged context.
+
+    ai-infra-handbooks "Paged KV cache", section "Paged attention": sequence b's
+    new tokens are q[qsl[b]:qsl[b+1]], the last n_b positions of a context of
+    seq_lens[b] tokens; new token j sits at position seq_lens[b] - n_b + j and
+    may see positions 0 .. that position (the lower-triangular mask offset by
+    seq_len - n).  K/V are gathered through the block table in logical order,
+    query head h reads KV head h // (H_q / H_kv), and each row is a plain
+    two-pass softmax-weighted sum.  Returns float64 [N, H_q, d]; when ``rows`` (a set
+    of row indices) is given, only those rows are computed and the others are NaN.
+    """
+    ntok, hq, d = q.shape
+    hkv = k_cache.shape[2]
+    grp = hq // hkv
+    s64 = float(np.float32(scale))
+    qf = to_f64(q, q_format)
+    out = np.full((ntok, hq, d), np.nan)
+    for b in range(len(seq_lens)):
+        start, end = int(query_start_loc[b]), int(query_start_loc[b + 1])
+        S, n = int(seq_lens[b]), end - start
+        want = [j for j in range(n) if rows is None or start + j in rows]
+        if not want:
+            continue
+        for g in range(hkv):
+            K = _gather(k_cache, block_tables[b], S, g, kv_format, k_scale, None)
+            V = _gather(v_cache, block_tables[b], S, g, kv_format, v_scale, None)
+            for j in want:
+                p = S - n + j                       # this token's position
+                for h in range(g * grp, (g + 1) * grp):
+                    logits = s64 * (K[:p + 1] @ qf[start + j, h])
+                    w = np.exp(logits - logits.max())
+                    out[start + j, h] = (w @ V[:p + 1]) / w.sum()
     return out
 
 

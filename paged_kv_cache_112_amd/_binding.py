@@ -20,7 +20,7 @@ PA_F32, PA_BF16, PA_FP8_E4M3 = 0, 1, 2
 # pa_kernel
 PA_KERNEL_AUTO, PA_KERNEL_VALU, PA_KERNEL_MFMA, PA_KERNEL_MFMA_PERSIST = 0, 1, 2, 3
 
-EXPORTED = ("pa_write_kv", "pa_copy_blocks", "pa_decode", "pa_decode_partition", "pa_merge",
+EXPORTED = ("pa_write_kv", "pa_copy_blocks", "pa_paged_attention", "pa_decode", "pa_decode_partition", "pa_merge",
             "pa_decode_workspace_bytes", "pa_default_partition_tokens", "pa_status_str")
 
 
@@ -55,6 +55,9 @@ def lib() -> ctypes.CDLL:
         L.pa_write_kv.restype = ctypes.c_int
         L.pa_copy_blocks.argtypes = [_vp, _vp, ctypes.POINTER(PaKvCache), _vp, _vp, _i32, _vp]
         L.pa_copy_blocks.restype = ctypes.c_int
+        L.pa_paged_attention.argtypes = [_vp, _i32, _i32, _i32, _i32, _vp, _vp, ctypes.POINTER(PaKvCache), _vp,
+                                         _i32, _vp, _vp, _i32, ctypes.c_float, _vp, _vp]
+        L.pa_paged_attention.restype = ctypes.c_int
         L.pa_decode.argtypes = _DECODE_ARGS
         L.pa_decode.restype = ctypes.c_int
         L.pa_decode_partition.argtypes = _DECODE_ARGS
@@ -89,6 +92,14 @@ def pa_write_kv(k, v, in_dtype, num_tokens, slot_mapping, k_cache, v_cache, cach
 
 def pa_copy_blocks(k_cache, v_cache, cache: PaKvCache, src, dst, num_pairs, stream) -> int:
     return lib().pa_copy_blocks(k_cache, v_cache, ctypes.byref(cache), src, dst, num_pairs, stream)
+
+
+def pa_paged_attention(q, q_dtype, num_tokens, num_seqs, num_q_heads, k_cache, v_cache, cache: PaKvCache,
+                       block_tables, max_blocks_per_seq, seq_lens, query_start_loc, max_query_len, scale, out,
+                       stream=None) -> int:
+    return lib().pa_paged_attention(q, q_dtype, num_tokens, num_seqs, num_q_heads, k_cache, v_cache,
+                                    ctypes.byref(cache), block_tables, max_blocks_per_seq, seq_lens,
+                                    query_start_loc, max_query_len, scale, out, stream)
 
 
 def pa_decode(q, q_dtype, num_seqs, num_q_heads, k_cache, v_cache, cache: PaKvCache, block_tables,
@@ -182,6 +193,27 @@ def copy_blocks(k_cache, v_cache, src, dst, stream=None) -> None:
         return
     desc = cache_desc(k_cache)
     check(pa_copy_blocks(_ptr(k_cache), _ptr(v_cache), desc, _ptr(src), _ptr(dst), src.numel(), _stream(stream)))
+
+
+def paged_attention(q, k_cache, v_cache, block_tables, seq_lens, query_start_loc, scale, max_query_len,
+                    out=None, k_scale: float = 1.0, v_scale: float = 1.0, stream=None):
+    """pa_paged_attention on torch tensors: q [N, H_q, d] bf16; seq_lens [B], query_start_loc [B+1] int32."""
+    if q.dim() != 3 or q.shape[2] != k_cache.shape[3]:
+        raise ValueError("q must be [num_tokens, num_q_heads, head_dim]")
+    if k_cache.shape != v_cache.shape or k_cache.dtype != v_cache.dtype:
+        raise ValueError("K and V pools must match")
+    for t in (block_tables, seq_lens, query_start_loc):
+        if t.dtype != _torch().int32:
+            raise ValueError("block_tables, seq_lens and query_start_loc must be int32")
+    if query_start_loc.numel() != seq_lens.numel() + 1:
+        raise ValueError("query_start_loc must have num_seqs + 1 entries")
+    if out is None:
+        out = _torch().empty_like(q)
+    desc = cache_desc(k_cache, k_scale, v_scale)
+    check(pa_paged_attention(_ptr(q), dtype_code(q), q.shape[0], seq_lens.numel(), q.shape[1], _ptr(k_cache),
+                             _ptr(v_cache), desc, _ptr(block_tables), block_tables.shape[1], _ptr(seq_lens),
+                             _ptr(query_start_loc), int(max_query_len), float(scale), _ptr(out), _stream(stream)))
+    return out
 
 
 def decode_workspace_bytes(num_seqs, num_q_heads, head_dim, max_context_len, partition_tokens=0) -> int:

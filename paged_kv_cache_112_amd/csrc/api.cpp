@@ -241,6 +241,52 @@ pa_status pa_copy_blocks(void* k_cache, void* v_cache, const pa_kv_cache* cache,
   return pa::launch_copy_blocks(a, static_cast<hipStream_t>(stream)) == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 
+pa_status pa_paged_attention(const void* q, int32_t q_dtype, int32_t num_tokens, int32_t num_seqs,
+                             int32_t num_q_heads, const void* k_cache, const void* v_cache,
+                             const pa_kv_cache* cache, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                             const int32_t* seq_lens, const int32_t* query_start_loc, int32_t max_query_len,
+                             float scale, void* out, void* stream) {
+  if (!q || !k_cache || !v_cache || !cache || !block_tables || !seq_lens || !query_start_loc || !out)
+    return PA_ERR_NULL;
+  if (const pa_status s = check_cache(cache); s != PA_OK) return s;
+  if (num_tokens < 0 || num_seqs < 0 || num_q_heads < 1 || max_blocks_per_seq < 1 || max_query_len < 0)
+    return PA_ERR_SHAPE;
+  if (num_q_heads % cache->num_kv_heads != 0 || !std::isfinite(scale)) return PA_ERR_SHAPE;
+  if (q_dtype != PA_BF16 || (cache->dtype != PA_BF16 && cache->dtype != PA_FP8_E4M3)) return PA_ERR_DTYPE;
+  const int32_t group = num_q_heads / cache->num_kv_heads;
+  if (group > 16 || (group & (group - 1)) != 0) return PA_ERR_UNSUPPORTED;
+  if (num_seqs > 65535) return PA_ERR_UNSUPPORTED;
+  if (num_tokens == 0 || num_seqs == 0 || max_query_len == 0) return PA_OK;
+  pa::AttnArgs a;
+  const int32_t esz = elem_bytes(cache->dtype);
+  a.q = q;
+  a.k_cache = static_cast<const uint8_t*>(k_cache);
+  a.v_cache = static_cast<const uint8_t*>(v_cache);
+  a.block_tables = block_tables;
+  a.seq_lens = seq_lens;
+  a.query_start_loc = query_start_loc;
+  a.out = out;
+  a.row_bytes = (int64_t)cache->num_kv_heads * cache->head_dim * esz;
+  a.block_bytes = a.row_bytes * cache->block_size;
+  a.num_tokens = num_tokens;
+  a.num_seqs = num_seqs;
+  a.num_q_heads = num_q_heads;
+  a.head_dim = cache->head_dim;
+  a.log2_group = log2i(group);
+  a.block_size = cache->block_size;
+  a.log2_bs = log2i(cache->block_size);
+  a.bt_stride = max_blocks_per_seq;
+  a.max_query_len = max_query_len;
+  a.num_kv_heads = cache->num_kv_heads;
+  a.kv_fmt = cache->dtype;
+  const float ks = cache->dtype == PA_FP8_E4M3 ? cache->k_scale : 1.0f;
+  a.qk_scale = scale * kLog2e * ks;
+  a.v_scale = cache->dtype == PA_FP8_E4M3 ? cache->v_scale : 1.0f;
+  const int64_t tiles = ((int64_t)max_query_len + (16 >> a.log2_group) - 1) / (16 >> a.log2_group);
+  if ((tiles + 3) / 4 * a.num_kv_heads > INT32_MAX) return PA_ERR_SHAPE;
+  return pa::launch_attention_mfma(a, static_cast<hipStream_t>(stream)) == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
 pa_status pa_decode_partition(const void* q, int32_t q_dtype, int32_t num_seqs, int32_t num_q_heads,
                               const void* k_cache, const void* v_cache, const pa_kv_cache* cache,
                               const int32_t* block_tables, int32_t max_blocks_per_seq,

@@ -80,7 +80,23 @@ struct CopyArgs {
   int32_t num_pairs;
 };
 
+struct AttnArgs {
+  const void* q;             // [num_tokens, H_q, D] bf16
+  const uint8_t* k_cache;
+  const uint8_t* v_cache;
+  const int32_t* block_tables;
+  const int32_t* seq_lens;         // [B]
+  const int32_t* query_start_loc;  // [B + 1]
+  void* out;                 // [num_tokens, H_q, D] bf16
+  int64_t row_bytes, block_bytes;
+  int32_t num_tokens, num_seqs, num_q_heads, head_dim, log2_group;
+  int32_t block_size, log2_bs, bt_stride, max_query_len;
+  int32_t num_kv_heads, kv_fmt;
+  float qk_scale, v_scale;
+};
+
 hipError_t launch_write_kv(const WriteArgs& a, hipStream_t stream);
+hipError_t launch_attention_mfma(const AttnArgs& a, hipStream_t stream);
 hipError_t launch_copy_blocks(const CopyArgs& a, hipStream_t stream);
 hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_decode_persist(const DecodeArgs& a, hipStream_t stream);

@@ -101,4 +101,39 @@ __device__ __forceinline__ void pv_tile(const VTile<FP8, D>& v, uint32_t p01, ui
   }
 }
 
+// O^T += V^T . P^T for one tile, the transposed form of pv_tile: A = V^T (row m =
+// head-dimension index, k = token) and B = the probabilities exactly as q.K^T left
+// them (k = token, column n = query head).  Lane (n, q4) supplies row n of block e as
+// column VEC*n + e of its four V rows.  Afterwards lane (n', q4') register r of O[e]
+// holds O[head n'][d = VEC*(4*q4' + r) + e]: every lane keeps its own head's values,
+// so a per-head rescale is a lane-local multiply.
+template <bool FP8, int D>
+__device__ __forceinline__ void pvt_tile(const VTile<FP8, D>& v, uint32_t p01, uint32_t p23, f32x4 (&O)[D / 16]) {
+  constexpr int VEC = D / 16;
+  const bf16x4 B = __builtin_bit_cast(bf16x4, u32x2{p01, p23});
+  uint32_t rw[4][VEC / 2];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    if constexpr (!FP8) {
+#pragma unroll
+      for (int c = 0; c < VEC / 2; ++c) rw[j][c] = v.w[j][c];
+    } else if constexpr (VEC == 8) {
+      rw[j][0] = e4m3x2_to_bf16x2(e4m3x2_lo(v.w[j][0]));
+      rw[j][1] = e4m3x2_to_bf16x2(e4m3x2_hi(v.w[j][0]));
+      rw[j][2] = e4m3x2_to_bf16x2(e4m3x2_lo(v.w[j][1]));
+      rw[j][3] = e4m3x2_to_bf16x2(e4m3x2_hi(v.w[j][1]));
+    } else {
+      rw[j][0] = e4m3x2_to_bf16x2(e4m3x2_lo(v.w[j]));
+      rw[j][1] = e4m3x2_to_bf16x2(e4m3x2_hi(v.w[j]));
+    }
+  }
+#pragma unroll
+  for (int c = 0; c < VEC / 2; ++c) {
+    const u32x2 even = {pack_lo_halves(rw[0][c], rw[1][c]), pack_lo_halves(rw[2][c], rw[3][c])};
+    const u32x2 odd = {pack_hi_halves(rw[0][c], rw[1][c]), pack_hi_halves(rw[2][c], rw[3][c])};
+    O[2 * c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(bf16x4, even), B, O[2 * c], 0, 0, 0);
+    O[2 * c + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(bf16x4, odd), B, O[2 * c + 1], 0, 0, 0);
+  }
+}
+
 }  // namespace pa

@@ -1,0 +1,148 @@
+"""pa_paged_attention (several new tokens per sequence, causal) against the oracle."""
+import json
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from conftest import GOLDEN
+from pools import POISON, STORAGE, from_dev, out_to_f64, to_dev
+from workloads import f32_to_bf16_bits, make_mq_config
+
+pytestmark = pytest.mark.gpu
+
+
+class MQ:
+    """Host pools (written by the oracle), tables and queries for one multi-query call."""
+
+    def __init__(self, seq_lens, qlens, hq, hkv, d, bs, kv="bf16", seed=0, tables=None, nb=None):
+        rng = np.random.default_rng(seed)
+        self.seq_lens = np.asarray(seq_lens, dtype=np.int32)
+        self.qsl = np.concatenate([[0], np.cumsum(qlens)]).astype(np.int32)
+        need = [-(-int(s) // bs) for s in seq_lens]
+        if tables is None:
+            nb = sum(need) + 3
+            perm = rng.permutation(nb)
+            tables, k = [], 0
+            for m in need:
+                tables.append(list(perm[k:k + m]))
+                k += m
+        width = max(max(need), 1)
+        self.bt = np.array([list(t) + [0] * (width - len(t)) for t in tables], dtype=np.int32)
+        self.kv, self.bs, self.d = kv, bs, d
+        self.kc = np.full((nb, bs, hkv, d), POISON[kv], dtype=STORAGE[kv])
+        self.vc = np.full_like(self.kc, POISON[kv])
+        self.ks = self.vs = 1.0
+        kvals = [rng.standard_normal((int(s), hkv, d)).astype(np.float32) for s in seq_lens]
+        vvals = [rng.standard_normal((int(s), hkv, d)).astype(np.float32) for s in seq_lens]
+        if kv == "e4m3":
+            bf = lambda x: (f32_to_bf16_bits(x).astype(np.uint32) << 16).view(np.float32)
+            self.ks = float(np.float32(max(np.abs(bf(x)).max() for x in kvals) / 448))
+            self.vs = float(np.float32(max(np.abs(bf(x)).max() for x in vvals) / 448))
+        for t, s, kk, vv in zip(tables, seq_lens, kvals, vvals):
+            slots = [t[p // bs] * bs + p % bs for p in range(int(s))]
+            oracle.write_kv(self.kc, self.vc, f32_to_bf16_bits(kk), f32_to_bf16_bits(vv), slots, kv, "bf16",
+                            self.ks, self.vs)
+        self.q = f32_to_bf16_bits(rng.standard_normal((int(self.qsl[-1]), hq, d)).astype(np.float32))
+
+    def run(self, scale, max_q=None):
+        import torch
+        import paged_kv_cache_112_amd as pa
+        qlens = np.diff(self.qsl)
+        out = pa.paged_attention(to_dev(self.q), to_dev(self.kc), to_dev(self.vc), to_dev(self.bt),
+                                 to_dev(self.seq_lens), to_dev(self.qsl), scale,
+                                 int(qlens.max()) if max_q is None else max_q, k_scale=self.ks, v_scale=self.vs)
+        torch.cuda.synchronize()
+        return out
+
+    def oracle(self, scale, rows=None):
+        return oracle.paged_attention(self.q, self.kc, self.vc, self.bt, self.seq_lens, self.qsl, scale, self.kv,
+                                      "bf16", self.ks, self.vs, rows=rows)
+
+
+@pytest.mark.parametrize("kv", ["bf16", "e4m3"])
+def test_printed_check(kv):
+    """The page's check: decode 1 of 37, a full prefill of 5, the last 8 of 20; its block tables."""
+    g = json.load(open(os.path.join(GOLDEN, "p2_round_robin_tables.json")))
+    m = MQ(g["seq_lens"], g["query_lens"], g["num_heads"], g["num_kv_heads"], g["head_dim"], g["block_size"],
+           kv, tables=g["tables"], nb=g["num_blocks"])
+    scale = g["head_dim"] ** -0.5
+    assert np.abs(out_to_f64(m.run(scale)) - m.oracle(scale)).max() <= 2e-2
+
+
+@pytest.mark.parametrize("hq,hkv,d", [(8, 8, 128), (16, 8, 64), (32, 8, 128), (32, 4, 64), (32, 2, 128)])
+@pytest.mark.parametrize("bs", [1, 4, 16, 64])
+def test_mixed_query_lengths(hq, hkv, d, bs):
+    seq_lens = [1, 5, 40, 300, 17, 130, 64]
+    qlens = [1, 5, 3, 300, 16, 17, 1]
+    m = MQ(seq_lens, qlens, hq, hkv, d, bs, seed=bs + hq + d)
+    scale = float(np.float32(1 / np.sqrt(d)))
+    assert np.abs(out_to_f64(m.run(scale)) - m.oracle(scale)).max() <= 2e-2
+
+
+@pytest.mark.parametrize("kv", ["bf16", "e4m3"])
+def test_peaky_scores(kv):
+    """A large scale makes each row nearly one-hot: a wrong key or mask shows as an O(1) error."""
+    m = MQ([70, 33, 129], [70, 9, 20], 32, 8, 128, 16, kv, seed=9)
+    scale = float(np.float32(8 / np.sqrt(128)))
+    assert np.abs(out_to_f64(m.run(scale)) - m.oracle(scale)).max() <= 2e-2
+
+
+def test_one_token_per_sequence_matches_decode():
+    import torch
+    import paged_kv_cache_112_amd as pa
+    seq_lens = [1, 16, 17, 255, 700]
+    m = MQ(seq_lens, [1] * len(seq_lens), 32, 8, 128, 16, seed=4)
+    scale = float(np.float32(1 / np.sqrt(128)))
+    mq = out_to_f64(m.run(scale))
+    dq = to_dev(m.q)
+    dec = pa.decode(dq, to_dev(m.kc), to_dev(m.vc), to_dev(m.bt), to_dev(m.seq_lens), scale,
+                    max_context_len=max(seq_lens))
+    torch.cuda.synchronize()
+    ref = oracle.decode(m.q, m.kc, m.vc, m.bt, m.seq_lens, scale, "bf16", "bf16")
+    assert np.abs(mq - ref).max() <= 2e-2
+    assert np.abs(out_to_f64(dec) - ref).max() <= 2e-2
+
+
+def test_sequences_with_no_new_tokens_and_bad_lengths_are_skipped():
+    """A sequence with no rows writes nothing; one claiming more new tokens than its context is skipped."""
+    import torch
+    import paged_kv_cache_112_amd as pa
+    m = MQ([40, 12, 30], [4, 0, 6], 16, 4, 64, 16, seed=5)
+    scale = 0.125
+    ref = m.oracle(scale)
+    out = m.run(scale)
+    assert np.abs(out_to_f64(out) - ref).max() <= 2e-2
+    bad = m.seq_lens.copy()
+    bad[2] = 3                                        # 6 new tokens but a context of 3
+    sentinel = torch.full_like(out, 7.0)
+    pa.paged_attention(to_dev(m.q), to_dev(m.kc), to_dev(m.vc), to_dev(m.bt), to_dev(bad), to_dev(m.qsl), scale,
+                       6, out=sentinel)
+    torch.cuda.synchronize()
+    got = out_to_f64(sentinel)
+    assert np.all(got[4:10] == 7.0)                   # rows of the inconsistent sequence untouched
+    assert np.abs(got[:4] - ref[:4]).max() <= 2e-2
+
+
+def test_chunk512_full_size_sampled_rows():
+    """llama3_8b_chunk512 at full size; every row of three sequences and spread rows of all, vs the oracle."""
+    import torch
+    import paged_kv_cache_112_amd as pa
+    w = make_mq_config("llama3_8b_chunk512")
+    rng = np.random.default_rng(w.seed)
+    shape = (w.num_blocks, w.block_size, w.num_kv_heads, w.head_dim)
+    kc = f32_to_bf16_bits(rng.standard_normal(shape).astype(np.float32))
+    vc = f32_to_bf16_bits(rng.standard_normal(shape).astype(np.float32))
+    q = f32_to_bf16_bits(w.mq_q_values())
+    qsl = w.query_start_loc()
+    out = pa.paged_attention(to_dev(q), to_dev(kc), to_dev(vc), to_dev(w.block_tables), to_dev(w.context_lens),
+                             to_dev(qsl), w.scale, int(w.query_lens.max()))
+    torch.cuda.synchronize()
+    got = out_to_f64(out)
+    rows = set(range(int(qsl[0]), int(qsl[0]) + 8)) | set(range(int(qsl[16]) + 500, int(qsl[17])))
+    rows |= set(int(r) for r in rng.choice(int(qsl[-1]), 40, replace=False))
+    rows |= {int(qsl[b + 1]) - 1 for b in range(w.num_seqs)}          # each sequence's last row
+    ref = oracle.paged_attention(q, kc, vc, w.block_tables, w.context_lens, qsl, w.scale, "bf16", "bf16", rows=rows)
+    idx = sorted(rows)
+    assert np.abs(got[idx] - ref[idx]).max() <= 2e-2

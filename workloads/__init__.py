@@ -10,7 +10,7 @@ from .lengths import p2_length_pairs, p2_context_lens
 from .values import (standard_normal_f32, f32_to_bf16_bits, bf16_bits_to_f32_exact,
                      BF16_NAN_BITS, E4M3_NAN_CODE)
 from .configs import (DecodeWorkload, make_config, CONFIG_NAMES, deal_tables,
-                      shared_prefix_tables)
+                      shared_prefix_tables, make_mq_config, MQ_CONFIG_NAMES)
 
 __all__ = [
     "BlockPool", "BlockManager", "slot_mapping_for", "build_step_tensors",
@@ -18,4 +18,5 @@ __all__ = [
     "standard_normal_f32", "f32_to_bf16_bits", "bf16_bits_to_f32_exact",
     "BF16_NAN_BITS", "E4M3_NAN_CODE",
     "DecodeWorkload", "make_config", "CONFIG_NAMES", "deal_tables", "shared_prefix_tables",
+    "make_mq_config", "MQ_CONFIG_NAMES",
 ]

@@ -82,6 +82,7 @@ class DecodeWorkload:
     shared_prefix_tokens: int = 0   # sequences 0..sharers-1 share this many leading tokens
     sharers: int = 0
     ref_count: np.ndarray = field(default=None)
+    query_lens: np.ndarray = field(default=None)  # multi-query workloads: new tokens per sequence
 
     @property
     def scale(self) -> float:
@@ -122,6 +123,17 @@ class DecodeWorkload:
         rng = np.random.default_rng([self.seed, stream, b])
         n = len(self.owned_positions(b))
         return rng.standard_normal((n, self.num_kv_heads, self.head_dim), dtype=np.float32)
+
+    # -- multi-query (several new tokens per sequence) ------------------------------
+    def query_start_loc(self) -> np.ndarray:
+        """int32 [B + 1]: sequence b's new tokens are rows qsl[b] .. qsl[b+1]-1."""
+        return np.concatenate([[0], np.cumsum(self.query_lens)]).astype(np.int32)
+
+    def mq_q_values(self) -> np.ndarray:
+        """float32 [sum(query_lens), H_q, d]: the new tokens' queries."""
+        rng = np.random.default_rng([self.seed, _Q])
+        n = int(np.sum(self.query_lens))
+        return rng.standard_normal((n, self.num_q_heads, self.head_dim), dtype=np.float32)
 
     def append_slots(self) -> np.ndarray:
         """slot_mapping of this step's write: position ctx-1 of every sequence (int32)."""
@@ -164,6 +176,23 @@ def _paged(name, B, hq, hkv, d, bs, kv, q, ctx, seed_perm, seed_vals):
 
 
 CONFIG_NAMES = ("tiny_f32", "llama3_8b_b64", "llama3_8b_long", "llama2_7b_mha", "llama3_8b_fp8_prefix")
+MQ_CONFIG_NAMES = ("llama3_8b_chunk512",)
+
+
+def make_mq_config(name: str) -> DecodeWorkload:
+    """Multi-query workloads: several new tokens per sequence, causal over the paged context.
+
+    llama3_8b_chunk512: 32 sequences with the lengths of the utilization experiment's
+    first 32 (prompt, output) pairs, each computing its last min(512, len) tokens -- the
+    final chunk of a chunked prefill -- on a Llama-3-8B layer (32/8 heads, d 128, bf16,
+    block 16, pool +10 %).
+    """
+    if name == "llama3_8b_chunk512":
+        ctx = p2_context_lens(32)
+        w = _paged(name, 32, 32, 8, 128, 16, "bf16", "bf16", ctx, 16, 106)
+        w.query_lens = np.minimum(512, w.context_lens).astype(np.int32)
+        return w
+    raise ValueError(f"unknown multi-query workload {name!r}")
 
 
 def make_config(name: str, block_size: int | None = None) -> DecodeWorkload:
