@@ -216,6 +216,66 @@ def bench_attention(args, torch, pa):
                       "timing": "HIP events around back-to-back calls, 8 pool copies in turn"}))
 
 
+def bench_graph_loop(args, torch, pa):
+    """The batch-64 decode loop with no host work per step: pa_slot_mapping (advancing the
+    lengths) -> pa_write_kv -> pa_decode, captured once per layer and replayed; each replay is
+    one more token for every sequence, on the next of 8 layer pools."""
+    from workloads import deal_tables, make_config
+    w = make_config(WORKLOAD)
+    dev = torch.device("cuda:0")
+    steps = max(args.steps, 8) // LAYERS * LAYERS
+    warm = max(args.warmup, 1)
+    B, hq, hkv, d, bs = w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim, w.block_size
+    room = (steps + warm) // LAYERS + 2                      # tokens each sequence gains
+    final = w.context_lens + room
+    need = int(sum(-(-int(c) // bs) for c in final))
+    nb = int(np.ceil(1.1 * need))
+    bt, _ = deal_tables(final, bs, np.random.default_rng(12).permutation(nb).astype(np.int32))
+    shape = (nb, bs, hkv, d)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(w.seed)
+    pools = [(torch.randn(shape, generator=gen, device=dev).to(torch.bfloat16),
+              torch.randn(shape, generator=gen, device=dev).to(torch.bfloat16)) for _ in range(LAYERS)]
+    dbt = torch.from_numpy(bt).to(dev)
+    ctx = torch.from_numpy((w.context_lens - 1).astype(np.int32)).to(dev)   # each replay of layer 0 advances
+    slots = torch.zeros(B, dtype=torch.int32, device=dev)
+    knew = torch.randn((B, hkv, d), generator=gen, device=dev).to(torch.bfloat16)
+    vnew = torch.randn((B, hkv, d), generator=gen, device=dev).to(torch.bfloat16)
+    q = torch.randn((B, hq, d), generator=gen, device=dev).to(torch.bfloat16)
+    out = torch.empty((B, hq, d), dtype=torch.bfloat16, device=dev)
+    max_ctx = int(final.max())
+    ws = pa.new_workspace(B, hq, d, max_ctx, 0, dev)
+
+    def model_step():
+        # one token for the whole model: the lengths advance once, every layer writes and decodes
+        pa.slot_mapping(dbt, ctx, bs, slots, advance=True)
+        for kc, vc in pools:
+            pa.write_kv(knew, vnew, slots, kc, vc)
+            pa.decode(q, kc, vc, dbt, ctx, w.scale, out=out, max_context_len=max_ctx, workspace=ws)
+
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        model_step()
+    for _ in range(warm):
+        graph.replay()
+    torch.cuda.synchronize()
+    s = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = steps // LAYERS
+    e0.record(s)
+    for _ in range(reps):
+        graph.replay()
+    e1.record(s)
+    torch.cuda.synchronize()
+    us_layer = e0.elapsed_time(e1) * 1e3 / (reps * LAYERS)
+    print(json.dumps({"metric": "device-side decode loop (slot mapping + write + decode per layer, graph replay)",
+                      "workload": WORKLOAD, "layers_per_graph": LAYERS, "model_steps": reps,
+                      "us_per_layer_step": round(us_layer, 2),
+                      "decode_tokens_per_s_per_layer": round(B / us_layer * 1e6, 1),
+                      "note": "lengths grow by one token per replay; tables pre-filled for the growth"}))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -229,10 +289,12 @@ def main():
     ap.add_argument("--block-size", type=int, default=None, help="block size for llama2_7b_mha")
     ap.add_argument("--copy-calibrate", type=int, default=0, metavar="MIB",
                     help="only copy MIB MiB with torch (a plain copy of known size, for counter scaling)")
-    ap.add_argument("--op", default="decode", choices=["decode", "copy_blocks", "write_prefill", "attention"],
+    ap.add_argument("--op", default="decode",
+                    choices=["decode", "copy_blocks", "write_prefill", "attention", "graph_loop"],
                     help="decode: the hot-path step (the headline line); copy_blocks: copy-on-write block "
                          "copies over the workload's pools; write_prefill: pa_write_kv of every context token; "
-                         "attention: multi-query paged attention on llama3_8b_chunk512")
+                         "attention: multi-query paged attention on llama3_8b_chunk512; graph_loop: the decode "
+                         "loop with device-side slot mapping, captured once and replayed")
     ap.add_argument("--contiguous", action="store_true",
                     help="identity-ordered block tables (each sequence's blocks adjacent): the contiguous comparator")
     args = ap.parse_args()
@@ -260,6 +322,8 @@ def main():
         build()
     if args.op == "attention":
         return bench_attention(args, torch, pa)
+    if args.op == "graph_loop":
+        return bench_graph_loop(args, torch, pa)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     w = make_config(args.workload, args.block_size) if args.workload == "llama2_7b_mha" else make_config(args.workload)

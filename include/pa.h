@@ -246,6 +246,31 @@ pa_status pa_paged_attention(const void* q, int32_t q_dtype, int32_t num_tokens,
                              const int32_t* seq_lens, const int32_t* query_start_loc, int32_t max_query_len,
                              float scale, void* out, void* stream);
 
+/* Device-side slot mapping for this step (and, optionally, the step's advance of
+ * the context lengths), so that a decode loop -- slot mapping, pa_write_kv,
+ * pa_decode -- needs no host work between steps and can be captured once in a
+ * HIP graph.  The pages have the engine rebuild these tensors on the host each
+ * step (LLM stack book, "From Python bookkeeping to the tensors the kernel
+ * actually takes"); the formula is theirs: new token j of sequence b, at position
+ * p = seq_lens[b] - n_b + j, goes to slot table[b][p / block_size] * block_size
+ * + p % block_size (ai-infra-handbooks "Paged KV cache", "Block tables and slot
+ * mapping").
+ *
+ *   block_tables  device int32 [num_seqs, max_blocks_per_seq]; the blocks for this
+ *                 step's positions must already be in the table (the host
+ *                 allocator appends them ahead of the steps it captures)
+ *   seq_lens      device int32 [num_seqs]; with advance != 0 each grows by n_b
+ *                 first (in place), so afterwards it counts this step's tokens
+ *   query_start_loc  device int32 [num_seqs + 1] rows of each sequence's new
+ *                 tokens, or NULL for one new token per sequence in row b
+ *   slot_mapping  device int32 [num_tokens], written for every new-token row; a
+ *                 position outside the table gets -1 (pa_write_kv skips it)
+ * Errors: PA_ERR_NULL, PA_ERR_SHAPE, PA_ERR_UNSUPPORTED (block_size not a power of
+ * two in 1..1024), PA_ERR_HIP.  num_seqs == 0 is a no-op returning PA_OK. */
+pa_status pa_slot_mapping(const int32_t* block_tables, int32_t max_blocks_per_seq, int32_t* seq_lens,
+                          const int32_t* query_start_loc, int32_t num_seqs, int32_t num_tokens, int32_t block_size,
+                          int32_t advance, int32_t* slot_mapping, void* stream);
+
 /* Static, human-readable name of a status code. */
 const char* pa_status_str(pa_status status);
 

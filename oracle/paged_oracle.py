@@ -23,6 +23,7 @@ What is computed (each function names its passage):
   * ``write_kv``: every new token i with slot_mapping[i] >= 0 lands in
     block slot // B at offset slot % B of the flat pool; a same-format write
     is a byte copy, an e4m3 pool stores the quantized value.
+  * ``slot_mapping``: each new token's slot from its sequence's block table.
   * ``copy_blocks``: copy-on-write's device step, whole physical blocks of both
     pools copied as stored.
   * ``decode``: for every sequence and query head, softmax(scale * q . K^T) V
@@ -199,6 +200,31 @@ def write_kv(k_cache: np.ndarray, v_cache: np.ndarray, k: np.ndarray, v: np.ndar
         blk, off = divmod(int(s), B)
         k_cache[blk, off] = kq[i]
         v_cache[blk, off] = vq[i]
+
+
+def slot_mapping(block_tables: np.ndarray, seq_lens, query_start_loc, block_size: int, num_tokens: int):
+    """Slots of this step's new tokens (int64 [num_tokens]).
+
+    New token j of sequence b sits at position p = seq_lens[b] - n_b + j and is
+    stored in logical block p // B at offset p % B, i.e. at slot
+    table[b][p // B] * B + p % B (ai-infra-handbooks "Paged KV cache", section
+    "Block tables and slot mapping"; int8ai.com, "How the Block Table Works").
+    ``query_start_loc`` None means one new token per sequence, in row b.  A
+    position outside the table gets -1.
+    """
+    out = np.full(num_tokens, -1, dtype=np.int64)
+    for b in range(len(seq_lens)):
+        if query_start_loc is None:
+            r0, n = b, 1
+        else:
+            r0, n = int(query_start_loc[b]), int(query_start_loc[b + 1]) - int(query_start_loc[b])
+        S = int(seq_lens[b])
+        for j in range(n):
+            p = S - n + j
+            lb, off = divmod(p, block_size)
+            if 0 <= r0 + j < num_tokens and p >= 0 and lb < block_tables.shape[1]:
+                out[r0 + j] = int(block_tables[b][lb]) * block_size + off
+    return out
 
 
 def copy_blocks(k_cache: np.ndarray, v_cache: np.ndarray, src, dst) -> None:

@@ -20,7 +20,7 @@ PA_F32, PA_BF16, PA_FP8_E4M3 = 0, 1, 2
 # pa_kernel
 PA_KERNEL_AUTO, PA_KERNEL_VALU, PA_KERNEL_MFMA, PA_KERNEL_MFMA_PERSIST = 0, 1, 2, 3
 
-EXPORTED = ("pa_write_kv", "pa_copy_blocks", "pa_paged_attention", "pa_decode", "pa_decode_partition", "pa_merge",
+EXPORTED = ("pa_write_kv", "pa_copy_blocks", "pa_paged_attention", "pa_slot_mapping", "pa_decode", "pa_decode_partition", "pa_merge",
             "pa_decode_workspace_bytes", "pa_default_partition_tokens", "pa_status_str")
 
 
@@ -55,6 +55,8 @@ def lib() -> ctypes.CDLL:
         L.pa_write_kv.restype = ctypes.c_int
         L.pa_copy_blocks.argtypes = [_vp, _vp, ctypes.POINTER(PaKvCache), _vp, _vp, _i32, _vp]
         L.pa_copy_blocks.restype = ctypes.c_int
+        L.pa_slot_mapping.argtypes = [_vp, _i32, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp]
+        L.pa_slot_mapping.restype = ctypes.c_int
         L.pa_paged_attention.argtypes = [_vp, _i32, _i32, _i32, _i32, _vp, _vp, ctypes.POINTER(PaKvCache), _vp,
                                          _i32, _vp, _vp, _i32, ctypes.c_float, _vp, _vp]
         L.pa_paged_attention.restype = ctypes.c_int
@@ -100,6 +102,12 @@ def pa_paged_attention(q, q_dtype, num_tokens, num_seqs, num_q_heads, k_cache, v
     return lib().pa_paged_attention(q, q_dtype, num_tokens, num_seqs, num_q_heads, k_cache, v_cache,
                                     ctypes.byref(cache), block_tables, max_blocks_per_seq, seq_lens,
                                     query_start_loc, max_query_len, scale, out, stream)
+
+
+def pa_slot_mapping(block_tables, max_blocks_per_seq, seq_lens, query_start_loc, num_seqs, num_tokens, block_size,
+                    advance, slot_mapping, stream=None) -> int:
+    return lib().pa_slot_mapping(block_tables, max_blocks_per_seq, seq_lens, query_start_loc, num_seqs, num_tokens,
+                                 block_size, advance, slot_mapping, stream)
 
 
 def pa_decode(q, q_dtype, num_seqs, num_q_heads, k_cache, v_cache, cache: PaKvCache, block_tables,
@@ -213,6 +221,17 @@ def paged_attention(q, k_cache, v_cache, block_tables, seq_lens, query_start_loc
     check(pa_paged_attention(_ptr(q), dtype_code(q), q.shape[0], seq_lens.numel(), q.shape[1], _ptr(k_cache),
                              _ptr(v_cache), desc, _ptr(block_tables), block_tables.shape[1], _ptr(seq_lens),
                              _ptr(query_start_loc), int(max_query_len), float(scale), _ptr(out), _stream(stream)))
+    return out
+
+
+def slot_mapping(block_tables, seq_lens, block_size, out, query_start_loc=None, advance=False, stream=None):
+    """pa_slot_mapping on torch int32 tensors; ``out`` (int32 [num_tokens]) receives the slots."""
+    for t in (block_tables, seq_lens, out) + ((query_start_loc,) if query_start_loc is not None else ()):
+        if t.dtype != _torch().int32:
+            raise ValueError("block_tables, seq_lens, query_start_loc and out must be int32")
+    check(pa_slot_mapping(_ptr(block_tables), block_tables.shape[1], _ptr(seq_lens),
+                          _ptr(query_start_loc) if query_start_loc is not None else None, seq_lens.numel(),
+                          out.numel(), int(block_size), 1 if advance else 0, _ptr(out), _stream(stream)))
     return out
 
 

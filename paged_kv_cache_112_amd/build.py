@@ -17,7 +17,7 @@ LIB_NAME = "libpa.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
 ARCH = "gfx950"
 
-SOURCES = ["api.cpp", "write_kv.hip", "copy_blocks.hip", "attention_mfma.hip", "decode_mfma.hip", "decode_persist.hip", "decode_valu.hip", "merge.hip"]
+SOURCES = ["api.cpp", "write_kv.hip", "copy_blocks.hip", "attention_mfma.hip", "step_tensors.hip", "decode_mfma.hip", "decode_persist.hip", "decode_valu.hip", "merge.hip"]
 
 # Packed-fp32 instructions are disabled on purpose; fp32 denormals are kept.  The
 # atomic optimizer is off: it turns the one-lane work-counter atomic of the persistent

@@ -287,6 +287,28 @@ pa_status pa_paged_attention(const void* q, int32_t q_dtype, int32_t num_tokens,
   return pa::launch_attention_mfma(a, static_cast<hipStream_t>(stream)) == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 
+pa_status pa_slot_mapping(const int32_t* block_tables, int32_t max_blocks_per_seq, int32_t* seq_lens,
+                          const int32_t* query_start_loc, int32_t num_seqs, int32_t num_tokens, int32_t block_size,
+                          int32_t advance, int32_t* slot_mapping, void* stream) {
+  if (!block_tables || !seq_lens || !slot_mapping) return PA_ERR_NULL;
+  if (num_seqs < 0 || num_tokens < 0 || max_blocks_per_seq < 1) return PA_ERR_SHAPE;
+  if (!query_start_loc && num_tokens < num_seqs) return PA_ERR_SHAPE;
+  if (block_size < 1 || block_size > 1024 || (block_size & (block_size - 1)) != 0) return PA_ERR_UNSUPPORTED;
+  if (num_seqs == 0) return PA_OK;
+  pa::SlotArgs a;
+  a.block_tables = block_tables;
+  a.seq_lens = seq_lens;
+  a.query_start_loc = query_start_loc;
+  a.slot_mapping = slot_mapping;
+  a.num_seqs = num_seqs;
+  a.num_tokens = num_tokens;
+  a.bt_stride = max_blocks_per_seq;
+  a.block_size = block_size;
+  a.log2_bs = log2i(block_size);
+  a.advance = advance != 0;
+  return pa::launch_slot_mapping(a, static_cast<hipStream_t>(stream)) == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
 pa_status pa_decode_partition(const void* q, int32_t q_dtype, int32_t num_seqs, int32_t num_q_heads,
                               const void* k_cache, const void* v_cache, const pa_kv_cache* cache,
                               const int32_t* block_tables, int32_t max_blocks_per_seq,

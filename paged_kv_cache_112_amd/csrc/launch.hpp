@@ -95,7 +95,16 @@ struct AttnArgs {
   float qk_scale, v_scale;
 };
 
+struct SlotArgs {
+  const int32_t* block_tables;
+  int32_t* seq_lens;               // advanced in place when `advance` is set
+  const int32_t* query_start_loc;  // NULL: one new token per sequence, row b
+  int32_t* slot_mapping;
+  int32_t num_seqs, num_tokens, bt_stride, block_size, log2_bs, advance;
+};
+
 hipError_t launch_write_kv(const WriteArgs& a, hipStream_t stream);
+hipError_t launch_slot_mapping(const SlotArgs& a, hipStream_t stream);
 hipError_t launch_attention_mfma(const AttnArgs& a, hipStream_t stream);
 hipError_t launch_copy_blocks(const CopyArgs& a, hipStream_t stream);
 hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t stream);

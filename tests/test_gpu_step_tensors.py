@@ -1,0 +1,125 @@
+"""Device-side step tensors: pa_slot_mapping against the oracle, and a decode loop
+(slot mapping with advance -> pa_write_kv -> pa_decode) captured once in a HIP graph
+and replayed step after step, checked against eager runs and the oracle."""
+import numpy as np
+import pytest
+
+import oracle
+from pools import POISON, STORAGE, from_dev, out_to_f64, to_dev
+from workloads import f32_to_bf16_bits
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("multi", [False, True])
+@pytest.mark.parametrize("advance", [False, True])
+@pytest.mark.parametrize("bs", [1, 4, 16, 256])
+def test_slot_mapping_matches_oracle(multi, advance, bs):
+    import torch
+    import paged_kv_cache_112_amd as pa
+    rng = np.random.default_rng(bs + 2 * multi + advance)
+    B, width = 37, 9
+    bt = rng.integers(0, 5000, (B, width), dtype=np.int32)
+    qlens = rng.integers(0, 6, B).astype(np.int32) if multi else np.ones(B, dtype=np.int32)
+    qsl = np.concatenate([[0], np.cumsum(qlens)]).astype(np.int32)
+    # lengths up to one block past the table, so some positions fall outside it (slot -1)
+    lens = rng.integers(0, width * bs + 2, B).astype(np.int32)
+    lens = np.maximum(lens, 0 if advance else qlens)
+    n = int(qsl[-1])
+    d_lens = to_dev(lens)
+    out = torch.full((n,), -7, dtype=torch.int32, device="cuda")
+    pa.slot_mapping(to_dev(bt), d_lens, bs, out, query_start_loc=to_dev(qsl) if multi else None, advance=advance)
+    torch.cuda.synchronize()
+    after = lens + qlens if advance else lens
+    ref = oracle.slot_mapping(bt, after, qsl if multi else None, bs, n)
+    assert np.array_equal(from_dev(out).astype(np.int64), ref)
+    assert np.array_equal(from_dev(d_lens), after)
+
+
+def _loop_setup(ctx0, steps, hq=32, hkv=8, d=128, bs=16, seed=11):
+    """Tables with room for `steps` more tokens per sequence; pools holding tokens 0..ctx0-1."""
+    rng = np.random.default_rng(seed)
+    B = len(ctx0)
+    final = np.asarray(ctx0) + steps
+    need = [-(-int(c) // bs) for c in final]
+    nb = sum(need) + 7
+    perm = rng.permutation(nb).astype(np.int32)
+    width = max(need)
+    bt = np.zeros((B, width), dtype=np.int32)
+    k = 0
+    for b, m in enumerate(need):
+        bt[b, :m] = perm[k:k + m]
+        k += m
+    kc = np.full((nb, bs, hkv, d), POISON["bf16"], dtype=np.uint16)
+    vc = np.full_like(kc, POISON["bf16"])
+    kv = [(f32_to_bf16_bits(rng.standard_normal((int(c), hkv, d)).astype(np.float32)),
+           f32_to_bf16_bits(rng.standard_normal((int(c), hkv, d)).astype(np.float32))) for c in final]
+    for b, c in enumerate(ctx0):
+        pos = np.arange(c)
+        oracle.write_kv(kc, vc, kv[b][0][:c], kv[b][1][:c], bt[b, pos // bs] * bs + pos % bs, "bf16", "bf16")
+    qs = [f32_to_bf16_bits(rng.standard_normal((B, hq, d)).astype(np.float32)) for _ in range(steps)]
+    return bt, kc, vc, kv, qs, final
+
+
+def test_graph_captured_decode_loop():
+    import torch
+    import paged_kv_cache_112_amd as pa
+    ctx0 = [1, 15, 16, 200, 511, 700, 33, 1024]
+    steps, bs, hq, d = 6, 16, 32, 128
+    bt, kc, vc, kv, qs, final = _loop_setup(ctx0, steps, bs=bs)
+    B = len(ctx0)
+    max_ctx = int(final.max())
+    scale = float(np.float32(1 / np.sqrt(d)))
+
+    def state():
+        s = dict(kc=to_dev(kc), vc=to_dev(vc), ctx=to_dev(np.asarray(ctx0, dtype=np.int32)),
+                 slots=torch.zeros(B, dtype=torch.int32, device="cuda"),
+                 knew=torch.zeros((B, 8, d), dtype=torch.bfloat16, device="cuda"),
+                 vnew=torch.zeros((B, 8, d), dtype=torch.bfloat16, device="cuda"),
+                 q=torch.zeros((B, hq, d), dtype=torch.bfloat16, device="cuda"),
+                 out=torch.zeros((B, hq, d), dtype=torch.bfloat16, device="cuda"),
+                 ws=pa.new_workspace(B, hq, d, max_ctx, 0, "cuda"))
+        return s
+
+    dbt = to_dev(bt)
+
+    def step(s):
+        pa.slot_mapping(dbt, s["ctx"], bs, s["slots"], advance=True)
+        pa.write_kv(s["knew"], s["vnew"], s["slots"], s["kc"], s["vc"])
+        pa.decode(s["q"], s["kc"], s["vc"], dbt, s["ctx"], scale, out=s["out"], max_context_len=max_ctx,
+                  workspace=s["ws"])
+
+    def feed(s, i):
+        # this step's inputs, copied in eagerly between replays
+        s["knew"].copy_(to_dev(np.stack([kv[b][0][ctx0[b] + i] for b in range(B)])))
+        s["vnew"].copy_(to_dev(np.stack([kv[b][1][ctx0[b] + i] for b in range(B)])))
+        s["q"].copy_(to_dev(qs[i]))
+
+    g_state, e_state = state(), state()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step(g_state)
+    torch.cuda.synchronize()
+    assert np.array_equal(from_dev(g_state["ctx"]), np.asarray(ctx0))      # capture ran nothing
+
+    okc, ovc = kc.copy(), vc.copy()
+    for i in range(steps):
+        feed(g_state, i)
+        graph.replay()
+        feed(e_state, i)
+        step(e_state)
+        torch.cuda.synchronize()
+        g_out, e_out = from_dev(g_state["out"]), from_dev(e_state["out"])
+        assert np.array_equal(g_out, e_out), f"replay {i} differs from the eager step"
+        # the oracle: write this step's tokens, decode over ctx0 + i + 1 tokens
+        lens = np.asarray(ctx0) + i + 1
+        for b in range(B):
+            p = int(lens[b]) - 1
+            oracle.write_kv(okc, ovc, kv[b][0][p:p + 1], kv[b][1][p:p + 1], [bt[b, p // bs] * bs + p % bs],
+                            "bf16", "bf16")
+        ref = oracle.decode(qs[i], okc, ovc, bt, lens, scale, "bf16", "bf16")
+        assert np.abs(out_to_f64(g_state["out"]) - ref).max() <= 2e-2
+    assert np.array_equal(from_dev(g_state["ctx"]), final)
+    assert np.array_equal(from_dev(g_state["kc"]), okc)
+    assert np.array_equal(from_dev(g_state["vc"]), ovc)
