@@ -287,6 +287,8 @@ def main():
     ap.add_argument("--workload", default=WORKLOAD,
                     choices=["llama3_8b_b64", "llama3_8b_long", "llama2_7b_mha", "llama3_8b_fp8_prefix"])
     ap.add_argument("--block-size", type=int, default=None, help="block size for llama2_7b_mha")
+    ap.add_argument("--kv-dtype", default=None, choices=["bf16", "e4m3", "i8"],
+                    help="pool format other than the workload's own (same lengths and tables)")
     ap.add_argument("--copy-calibrate", type=int, default=0, metavar="MIB",
                     help="only copy MIB MiB with torch (a plain copy of known size, for counter scaling)")
     ap.add_argument("--op", default="decode",
@@ -327,6 +329,8 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     w = make_config(args.workload, args.block_size) if args.workload == "llama2_7b_mha" else make_config(args.workload)
+    if args.kv_dtype and args.kv_dtype != w.kv_dtype:
+        w = w.with_dtypes(args.kv_dtype, "bf16", name=f"{w.name}-{args.kv_dtype}")
     if args.contiguous:
         from workloads import deal_tables
         w.block_tables, _ = deal_tables(w.context_lens, w.block_size, np.arange(w.num_blocks, dtype=np.int32))
@@ -342,9 +346,10 @@ def main():
 
     # ---- inputs resident in HBM: pools filled with every token but this step's ---------------
     # Values are seeded N(0,1) drawn on the device (bf16), written through pa_write_kv.
-    fp8 = w.kv_dtype == "e4m3"
-    kv_dtype = torch.uint8 if fp8 else torch.bfloat16
-    k_scale, v_scale = (float(np.float32(4.8 / 448)), float(np.float32(4.8 / 448))) if fp8 else (1.0, 1.0)
+    fp8 = w.kv_dtype in ("e4m3", "i8")              # one-byte pools
+    kv_dtype = {"e4m3": torch.uint8, "i8": torch.int8}.get(w.kv_dtype, torch.bfloat16)
+    qmax = 448.0 if w.kv_dtype == "e4m3" else 127.0
+    k_scale, v_scale = (float(np.float32(4.8 / qmax)), float(np.float32(4.8 / qmax))) if fp8 else (1.0, 1.0)
     shape = (w.num_blocks, bs, hkv, d)
     k0 = torch.zeros(shape, dtype=kv_dtype, device=dev)
     v0 = torch.zeros(shape, dtype=kv_dtype, device=dev)
@@ -484,7 +489,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16 q / e4m3 kv" if fp8 else "bf16",
+        "dtype": f"bf16 q / {w.kv_dtype} kv" if fp8 else "bf16",
         "data": "synthetic",
         "config": {"workload": w.name, "batch": B, "num_q_heads": hq, "num_kv_heads": hkv, "head_dim": d,
                    "block_size": bs, "sum_context": w.total_tokens, "max_context": max_ctx,

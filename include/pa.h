@@ -60,14 +60,15 @@ typedef enum pa_status {
 typedef enum pa_dtype {
   PA_F32 = 0,             /* IEEE binary32 */
   PA_BF16 = 1,            /* bfloat16: the upper 16 bits of a binary32 */
-  PA_FP8_E4M3 = 2         /* OCP E4M3FN (bias 7, no infinity, S.1111.111 = NaN, max 448) */
+  PA_FP8_E4M3 = 2,        /* OCP E4M3FN (bias 7, no infinity, S.1111.111 = NaN, max 448) */
+  PA_INT8 = 3             /* signed 8-bit integer code, symmetric: -127 .. 127 */
 } pa_dtype;
 
-/* Describes both pools.  k_scale / v_scale are used only for PA_FP8_E4M3
- * pools: the real value of a stored code c is e4m3(c) * scale (one fp32 scale
- * per pool).  The pages only say an fp8 cache halves the bytes per element
- * (LLM stack book, "The libraries that implement this"); the per-tensor scale
- * is this library's reading of it. */
+/* Describes both pools.  k_scale / v_scale are used only for the one-byte pools
+ * (PA_FP8_E4M3, PA_INT8): the real value of a stored code c is value(c) * scale,
+ * one fp32 scale per pool.  The pages only say that quantizing the cache to fp8 or
+ * int8 halves the bytes per element (LLM stack book, "The libraries that implement
+ * this" and "Why it matters"); the per-tensor scale is this library's reading. */
 typedef struct pa_kv_cache {
   int64_t num_blocks;     /* physical blocks in each pool, >= 1 */
   int32_t block_size;     /* tokens per block: a power of two, 1..1024 */
@@ -91,7 +92,9 @@ typedef struct pa_kv_cache {
  *   in_dtype      == cache->dtype for PA_F32 / PA_BF16 pools (bit-exact copy);
  *                 PA_BF16 or PA_F32 for a PA_FP8_E4M3 pool, which stores
  *                 RNE-saturating e4m3(fp32(x * fp32(1 / scale))), NaN -> NaN
- *                 code with the input's sign
+ *                 code with the input's sign; PA_BF16 or PA_F32 for a PA_INT8
+ *                 pool, which stores clamp(rint(fp32(x * fp32(1 / scale))),
+ *                 -127, 127) with ties to even, NaN -> 0
  *   slot_mapping  device int32 [num_tokens]; slots must be distinct and
  *                 < num_blocks * block_size
  *   k_cache, v_cache  device pools, written in place
@@ -139,10 +142,10 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t 
 
 /* Kernel selection for pa_decode / pa_decode_partition. */
 typedef enum pa_kernel {
-  PA_KERNEL_AUTO = 0,      /* matrix-core path for bf16/e4m3 pools, vector path for f32 */
+  PA_KERNEL_AUTO = 0,      /* matrix-core path for bf16/e4m3/int8 pools, vector path for f32 */
   PA_KERNEL_VALU = 1,      /* vector-ALU path (all formats, query-head group <= 8) */
   PA_KERNEL_MFMA = 2,      /* matrix-core path, one workgroup per (sequence, partition, up to
-                              four KV heads) (bf16 q with bf16 or e4m3 pools, group <= 16) */
+                              four KV heads) (bf16 q with bf16, e4m3 or int8 pools, group <= 16) */
   PA_KERNEL_MFMA_PERSIST = 3 /* matrix-core path, persistent workgroups that each stream a
                               contiguous range of work units (same inputs; num_seqs > 1024
                               runs PA_KERNEL_MFMA instead) */
@@ -158,7 +161,7 @@ typedef enum pa_kernel {
  * Kernel Overview").  A sequence with context_lens[b] == 0 gets zeros.
  *
  *   q             device [num_seqs, num_q_heads, head_dim] of q_dtype
- *                 (PA_F32 with an f32 pool; PA_BF16 with a bf16 or e4m3 pool)
+ *                 (PA_F32 with an f32 pool; PA_BF16 with a bf16, e4m3 or int8 pool)
  *   k_cache, v_cache, cache   the pools (read only)
  *   block_tables  device int32 [num_seqs, max_blocks_per_seq]; entries at index
  *                 >= ceil(context_lens[b] / block_size) are never read
@@ -229,7 +232,7 @@ pa_status pa_merge(const void* workspace, size_t workspace_bytes, int32_t num_se
  * seq_len - num_new; the result equals contiguous attention).
  *
  *   q, out        device [num_tokens, num_q_heads, head_dim] bf16 (q_dtype PA_BF16)
- *   cache         a PA_BF16 or PA_FP8_E4M3 pool; num_q_heads / num_kv_heads in
+ *   cache         a PA_BF16, PA_FP8_E4M3 or PA_INT8 pool; num_q_heads / num_kv_heads in
  *                 {1, 2, 4, 8, 16}
  *   block_tables  device int32 [num_seqs, max_blocks_per_seq]
  *   seq_lens      device int32 [num_seqs], context length including the new tokens

@@ -12,6 +12,7 @@ sign/exponent/mantissa fields.  Arrays are passed as raw storage:
   * "f32"  -> float32 values
   * "bf16" -> uint16 bit patterns
   * "e4m3" -> uint8 codes (values are code * per-tensor scale)
+  * "i8"   -> int8 codes (values are code * per-tensor scale)
 
 Caches have the layout [num_blocks, block_size, H_kv, d_h] (LLM stack book
 "4.6 PagedAttention & KV-Cache Memory Management", section "Block Tables, the
@@ -59,8 +60,8 @@ import math
 
 import numpy as np
 
-FORMATS = ("f32", "bf16", "e4m3")
-ELEM_BYTES = {"f32": 4, "bf16": 2, "e4m3": 1}
+FORMATS = ("f32", "bf16", "e4m3", "i8")
+ELEM_BYTES = {"f32": 4, "bf16": 2, "e4m3": 1, "i8": 1}
 E4M3_MAX = 448.0
 LOG2E = 1.4426950408889634
 
@@ -150,6 +151,21 @@ def e4m3_quantize(x_f32: np.ndarray, scale: float) -> np.ndarray:
     return e4m3_encode(y)
 
 
+def int8_quantize(x_f32: np.ndarray, scale: float) -> np.ndarray:
+    """Stored int8 code of real value x for a pool with per-tensor scale.
+
+    The pages say only that quantizing the cache to int8 halves the bytes per
+    element (LLM stack book, "Why it matters"); the reading here is symmetric
+    per-tensor quantization: y = fp32(x * fp32(1/scale)) (one fp32 rounding),
+    then round to nearest with ties to even and clamp to [-127, 127]; NaN -> 0.
+    """
+    inv = np.float32(1.0) / np.float32(scale)
+    with np.errstate(over="ignore", invalid="ignore"):
+        y = (np.asarray(x_f32, dtype=np.float32) * inv).astype(np.float64)
+    code = np.clip(np.rint(np.nan_to_num(y, nan=0.0, posinf=127.0, neginf=-127.0)), -127, 127)
+    return code.astype(np.int8)
+
+
 def to_f64(arr: np.ndarray, fmt: str, scale: float = 1.0) -> np.ndarray:
     """Decode stored values to float64 (e4m3 codes are multiplied by their scale)."""
     if fmt == "f32":
@@ -158,6 +174,8 @@ def to_f64(arr: np.ndarray, fmt: str, scale: float = 1.0) -> np.ndarray:
         return bf16_to_f64(arr)
     if fmt == "e4m3":
         return e4m3_to_f64(arr) * float(np.float32(scale))
+    if fmt == "i8":
+        return np.asarray(arr, dtype=np.int8).astype(np.float64) * float(np.float32(scale))
     raise ValueError(fmt)
 
 
@@ -183,13 +201,16 @@ def write_kv(k_cache: np.ndarray, v_cache: np.ndarray, k: np.ndarray, v: np.ndar
     actually takes": the pool viewed as [num_blocks * B, H_kv, d_h]; "Putting It
     Together": divmod of the slot).  A negative slot skips the token.  When
     the pool format equals the input format the row is copied bit for bit;
-    an e4m3 pool stores e4m3_quantize(row, scale).
+    an e4m3 pool stores e4m3_quantize(row, scale), an int8 pool int8_quantize.
     """
     B = k_cache.shape[1]
     slots = np.asarray(slot_mapping, dtype=np.int64)
     if kv_format == "e4m3":
         kq = e4m3_quantize(_as_f32(k, in_format), k_scale)
         vq = e4m3_quantize(_as_f32(v, in_format), v_scale)
+    elif kv_format == "i8":
+        kq = int8_quantize(_as_f32(k, in_format), k_scale)
+        vq = int8_quantize(_as_f32(v, in_format), v_scale)
     else:
         if kv_format != in_format:
             raise ValueError("a non-fp8 pool takes input of its own format")

@@ -16,7 +16,7 @@ LIB_PATH = os.path.join(HERE, "libpa.so")
 # pa_status
 PA_OK, PA_ERR_NULL, PA_ERR_SHAPE, PA_ERR_DTYPE, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_HIP = range(7)
 # pa_dtype
-PA_F32, PA_BF16, PA_FP8_E4M3 = 0, 1, 2
+PA_F32, PA_BF16, PA_FP8_E4M3, PA_INT8 = 0, 1, 2, 3
 # pa_kernel
 PA_KERNEL_AUTO, PA_KERNEL_VALU, PA_KERNEL_MFMA, PA_KERNEL_MFMA_PERSIST = 0, 1, 2, 3
 
@@ -156,6 +156,8 @@ def dtype_code(t) -> int:
         return PA_BF16
     if t.dtype in (torch.uint8, getattr(torch, "float8_e4m3fn", torch.uint8)):
         return PA_FP8_E4M3
+    if t.dtype == torch.int8:
+        return PA_INT8
     raise TypeError(f"unsupported dtype {t.dtype}")
 
 

@@ -32,6 +32,8 @@ int32_t log2i(int64_t x) {
 }
 
 int32_t elem_bytes(int32_t fmt) { return fmt == PA_F32 ? 4 : fmt == PA_BF16 ? 2 : 1; }
+// one-byte pools store code * per-pool scale
+bool is_scaled(int32_t fmt) { return fmt == PA_FP8_E4M3 || fmt == PA_INT8; }
 
 bool valid_partition(int32_t p) {
   return p == 16 || p == 32 || p == 64 || p == 128 || p == 256 || p == 512 || p == 1024;
@@ -64,10 +66,10 @@ bool workspace_layout(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim, i
 pa_status check_cache(const pa_kv_cache* c) {
   if (!c) return PA_ERR_NULL;
   if (c->num_blocks < 1 || c->num_kv_heads < 1 || c->block_size < 1) return PA_ERR_SHAPE;
-  if (c->dtype != PA_F32 && c->dtype != PA_BF16 && c->dtype != PA_FP8_E4M3) return PA_ERR_DTYPE;
+  if (c->dtype != PA_F32 && c->dtype != PA_BF16 && c->dtype != PA_FP8_E4M3 && c->dtype != PA_INT8) return PA_ERR_DTYPE;
   if (!is_pow2(c->block_size) || c->block_size > 1024) return PA_ERR_UNSUPPORTED;
   if (c->head_dim != 64 && c->head_dim != 128) return PA_ERR_UNSUPPORTED;
-  if (c->dtype == PA_FP8_E4M3) {
+  if (is_scaled(c->dtype)) {
     if (!(c->k_scale > 0.f) || !(c->v_scale > 0.f) || !std::isfinite(c->k_scale) || !std::isfinite(c->v_scale))
       return PA_ERR_SHAPE;
   }
@@ -94,7 +96,7 @@ pa_status prepare_decode(const void* q, int32_t q_dtype, int32_t num_seqs, int32
   if (!std::isfinite(scale)) return PA_ERR_SHAPE;
   if (num_seqs > 65535) return PA_ERR_UNSUPPORTED;
   const bool f32_pair = q_dtype == PA_F32 && cache->dtype == PA_F32;
-  const bool bf16_q = q_dtype == PA_BF16 && (cache->dtype == PA_BF16 || cache->dtype == PA_FP8_E4M3);
+  const bool bf16_q = q_dtype == PA_BF16 && cache->dtype != PA_F32;
   if (!f32_pair && !bf16_q) return PA_ERR_DTYPE;
   const int32_t group = num_q_heads / cache->num_kv_heads;
   const int32_t P = partition_tokens == 0 ? kDefaultPartition : partition_tokens;
@@ -145,9 +147,9 @@ pa_status prepare_decode(const void* q, int32_t q_dtype, int32_t num_seqs, int32
   a.head_groups = cache->num_kv_heads / a.heads_per_wg;
   a.q_fmt = q_dtype;
   a.kv_fmt = cache->dtype;
-  const float ks = cache->dtype == PA_FP8_E4M3 ? cache->k_scale : 1.0f;
+  const float ks = is_scaled(cache->dtype) ? cache->k_scale : 1.0f;
   a.qk_scale = scale * kLog2e * ks;
-  a.v_scale = cache->dtype == PA_FP8_E4M3 ? cache->v_scale : 1.0f;
+  a.v_scale = is_scaled(cache->dtype) ? cache->v_scale : 1.0f;
   a.dense = num_seqs <= pa::kDenseMaxSeqs && (int64_t)ws.parts * a.head_groups * num_seqs < INT32_MAX;
   call->kernel = k;
   call->ws = ws;
@@ -207,6 +209,8 @@ pa_status pa_write_kv(const void* k, const void* v, int32_t in_dtype, int32_t nu
   else if (cache->dtype == PA_F32 && in_dtype == PA_F32) mode = 1;
   else if (cache->dtype == PA_FP8_E4M3 && in_dtype == PA_BF16) mode = 2;
   else if (cache->dtype == PA_FP8_E4M3 && in_dtype == PA_F32) mode = 3;
+  else if (cache->dtype == PA_INT8 && in_dtype == PA_BF16) mode = 4;
+  else if (cache->dtype == PA_INT8 && in_dtype == PA_F32) mode = 5;
   else return PA_ERR_DTYPE;
   if (num_tokens == 0) return PA_OK;
   pa::WriteArgs a;
@@ -218,8 +222,8 @@ pa_status pa_write_kv(const void* k, const void* v, int32_t in_dtype, int32_t nu
   a.num_tokens = num_tokens;
   a.row_elems = cache->num_kv_heads * cache->head_dim;
   a.mode = mode;
-  a.inv_k = cache->dtype == PA_FP8_E4M3 ? 1.0f / cache->k_scale : 1.0f;
-  a.inv_v = cache->dtype == PA_FP8_E4M3 ? 1.0f / cache->v_scale : 1.0f;
+  a.inv_k = is_scaled(cache->dtype) ? 1.0f / cache->k_scale : 1.0f;
+  a.inv_v = is_scaled(cache->dtype) ? 1.0f / cache->v_scale : 1.0f;
   return pa::launch_write_kv(a, static_cast<hipStream_t>(stream)) == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 
@@ -252,7 +256,7 @@ pa_status pa_paged_attention(const void* q, int32_t q_dtype, int32_t num_tokens,
   if (num_tokens < 0 || num_seqs < 0 || num_q_heads < 1 || max_blocks_per_seq < 1 || max_query_len < 0)
     return PA_ERR_SHAPE;
   if (num_q_heads % cache->num_kv_heads != 0 || !std::isfinite(scale)) return PA_ERR_SHAPE;
-  if (q_dtype != PA_BF16 || (cache->dtype != PA_BF16 && cache->dtype != PA_FP8_E4M3)) return PA_ERR_DTYPE;
+  if (q_dtype != PA_BF16 || cache->dtype == PA_F32) return PA_ERR_DTYPE;
   const int32_t group = num_q_heads / cache->num_kv_heads;
   if (group > 16 || (group & (group - 1)) != 0) return PA_ERR_UNSUPPORTED;
   if (num_seqs > 65535) return PA_ERR_UNSUPPORTED;
@@ -279,9 +283,9 @@ pa_status pa_paged_attention(const void* q, int32_t q_dtype, int32_t num_tokens,
   a.max_query_len = max_query_len;
   a.num_kv_heads = cache->num_kv_heads;
   a.kv_fmt = cache->dtype;
-  const float ks = cache->dtype == PA_FP8_E4M3 ? cache->k_scale : 1.0f;
+  const float ks = is_scaled(cache->dtype) ? cache->k_scale : 1.0f;
   a.qk_scale = scale * kLog2e * ks;
-  a.v_scale = cache->dtype == PA_FP8_E4M3 ? cache->v_scale : 1.0f;
+  a.v_scale = is_scaled(cache->dtype) ? cache->v_scale : 1.0f;
   const int64_t tiles = ((int64_t)max_query_len + (16 >> a.log2_group) - 1) / (16 >> a.log2_group);
   if ((tiles + 3) / 4 * a.num_kv_heads > INT32_MAX) return PA_ERR_SHAPE;
   return pa::launch_attention_mfma(a, static_cast<hipStream_t>(stream)) == hipSuccess ? PA_OK : PA_ERR_HIP;

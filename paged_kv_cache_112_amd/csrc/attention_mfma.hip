@@ -36,9 +36,9 @@ __device__ __forceinline__ int32_t attn_load_uniform(const int32_t* p) {
   return *(const __attribute__((address_space(4))) int32_t*)p;
 }
 
-template <bool FP8, int D, bool BIGBS>
+template <int KF, int D, bool BIGBS>
 __global__ __launch_bounds__(256) void attention_mfma_kernel(const AttnArgs a) {
-  constexpr int ESZ = FP8 ? 1 : 2;
+  constexpr int ESZ = byte_fmt(KF) ? 1 : 2;
   constexpr int VEC = D / 16;
   constexpr int NKK = D / 32;
   const int kvh = blockIdx.x % a.num_kv_heads;
@@ -73,7 +73,7 @@ __global__ __launch_bounds__(256) void attention_mfma_kernel(const AttnArgs a) {
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
       u32x4 w = {0u, 0u, 0u, 0u};
-      if (qvalid) w = ld16(qrow + q_col<FP8, D>(kk, q4));
+      if (qvalid) w = ld16(qrow + q_col<KF, D>(kk, q4));
       qB[kk] = __builtin_bit_cast(bf16x8, w);
     }
   }
@@ -92,18 +92,18 @@ __global__ __launch_bounds__(256) void attention_mfma_kernel(const AttnArgs a) {
     return (int64_t)blk * a.block_bytes + (int64_t)(tc & bs_mask) * a.row_bytes;
   };
   auto load_k = [&](int kt) {
-    KTile<FP8, D> t;
+    KTile<KF, D> t;
     const uint8_t* p = kbase + row_off(16 * kt + n, kt) + 16 * q4;
 #pragma unroll
-    for (int j = 0; j < KTile<FP8, D>::N; ++j) t.w[j] = ld16(p + 64 * j);
+    for (int j = 0; j < KTile<KF, D>::N; ++j) t.w[j] = ld16(p + 64 * j);
     return t;
   };
   auto load_v = [&](int kt) {
-    VTile<FP8, D> t;
+    VTile<KF, D> t;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const uint8_t* p = vbase + row_off(16 * kt + 4 * q4 + j, kt) + n * VEC * ESZ;
-      t.w[j] = *reinterpret_cast<const typename VTile<FP8, D>::W*>(p);
+      t.w[j] = *reinterpret_cast<const typename VTile<KF, D>::W*>(p);
     }
     return t;
   };
@@ -112,16 +112,16 @@ __global__ __launch_bounds__(256) void attention_mfma_kernel(const AttnArgs a) {
 #pragma unroll
   for (int e = 0; e < VEC; ++e) O[e] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m = -INFINITY, lsum = 0.f;
-  KTile<FP8, D> kc = load_k(0);
-  VTile<FP8, D> vc = load_v(0);
+  KTile<KF, D> kc = load_k(0);
+  VTile<KF, D> vc = load_v(0);
   for (int kt = 0; kt < nkt; ++kt) {
-    KTile<FP8, D> kn;
-    VTile<FP8, D> vn;
+    KTile<KF, D> kn;
+    VTile<KF, D> vn;
     if (kt + 1 < nkt) {                             // next tile in flight while this one computes
       kn = load_k(kt + 1);
       vn = load_v(kt + 1);
     }
-    const f32x4 s = qk_tile<FP8, D>(kc, qB);
+    const f32x4 s = qk_tile<KF, D>(kc, qB);
     float x[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -144,7 +144,7 @@ __global__ __launch_bounds__(256) void attention_mfma_kernel(const AttnArgs a) {
     lsum = lsum * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
 #pragma unroll
     for (int e = 0; e < VEC; ++e) O[e] *= alpha;
-    pvt_tile<FP8, D>(vc, pack_bf16(p[0], p[1]), pack_bf16(p[2], p[3]), O);
+    pvt_tile<KF, D>(vc, pack_bf16(p[0], p[1]), pack_bf16(p[2], p[3]), O);
     if (kt + 1 < nkt) {
       kc = kn;
       vc = vn;
@@ -169,10 +169,10 @@ __global__ __launch_bounds__(256) void attention_mfma_kernel(const AttnArgs a) {
   }
 }
 
-template <bool FP8, int D>
+template <int KF, int D>
 static void launch_d(const AttnArgs& a, dim3 grid, dim3 block, hipStream_t s) {
-  if (a.block_size >= 16) hipLaunchKernelGGL((attention_mfma_kernel<FP8, D, true>), grid, block, 0, s, a);
-  else hipLaunchKernelGGL((attention_mfma_kernel<FP8, D, false>), grid, block, 0, s, a);
+  if (a.block_size >= 16) hipLaunchKernelGGL((attention_mfma_kernel<KF, D, true>), grid, block, 0, s, a);
+  else hipLaunchKernelGGL((attention_mfma_kernel<KF, D, false>), grid, block, 0, s, a);
 }
 
 hipError_t launch_attention_mfma(const AttnArgs& a, hipStream_t s) {
@@ -180,9 +180,13 @@ hipError_t launch_attention_mfma(const AttnArgs& a, hipStream_t s) {
   const int tiles = (a.max_query_len + T - 1) / T;
   const dim3 grid((unsigned)(((tiles + kAttnWaves - 1) / kAttnWaves) * a.num_kv_heads), (unsigned)a.num_seqs);
   const dim3 block((unsigned)(kWave * kAttnWaves));
-  const bool fp8 = a.kv_fmt == kE4m3;
-  if (a.head_dim == 128) fp8 ? launch_d<true, 128>(a, grid, block, s) : launch_d<false, 128>(a, grid, block, s);
-  else fp8 ? launch_d<true, 64>(a, grid, block, s) : launch_d<false, 64>(a, grid, block, s);
+  const bool d128 = a.head_dim == 128;
+  switch (a.kv_fmt) {
+    case kBf16: d128 ? launch_d<kFmtBf16, 128>(a, grid, block, s) : launch_d<kFmtBf16, 64>(a, grid, block, s); break;
+    case kE4m3: d128 ? launch_d<kFmtE4m3, 128>(a, grid, block, s) : launch_d<kFmtE4m3, 64>(a, grid, block, s); break;
+    case kInt8: d128 ? launch_d<kFmtInt8, 128>(a, grid, block, s) : launch_d<kFmtInt8, 64>(a, grid, block, s); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

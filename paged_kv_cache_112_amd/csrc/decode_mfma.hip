@@ -78,7 +78,7 @@ __device__ __forceinline__ int32_t load_uniform(const int32_t* p) {
 // of the wave holds one head's output in register 0.
 __device__ __forceinline__ int head_of_column(int n) { return 4 * (n & 3) + (n >> 2); }
 
-template <bool FP8, int D, int PT, bool BIGBS>
+template <int KF, int D, int PT, bool BIGBS>
 __global__ __launch_bounds__(PA_WG_THREADS) __attribute__((amdgpu_waves_per_eu(PA_MIN_WAVES_PER_EU, PA_MAX_WAVES_PER_EU)))
 void decode_mfma_kernel(const DecodeArgs a) {
   // A partition of P = 16 * PT * W tokens is shared by W waves per KV head: wave w
@@ -86,10 +86,10 @@ void decode_mfma_kernel(const DecodeArgs a) {
   // are combined through LDS before anything is written.
   const int W = a.waves_per_head;
   const int P = 16 * PT * W;
-  constexpr int ESZ = FP8 ? 1 : 2;
+  constexpr int ESZ = byte_fmt(KF) ? 1 : 2;
   constexpr int VEC = D / 16;
   constexpr int NKK = D / 32;
-  constexpr int DEPTH = FP8 ? PA_MFMA_DEPTH_FP8 : PA_MFMA_DEPTH;
+  constexpr int DEPTH = byte_fmt(KF) ? PA_MFMA_DEPTH_FP8 : PA_MFMA_DEPTH;
   constexpr int KD = PT < DEPTH ? PT : DEPTH;
   __shared__ int32_t tbl[BIGBS ? 1 : kMaxPartitionTokens];
   extern __shared__ float xs[];     // combine area, W > 1 only
@@ -166,27 +166,27 @@ void decode_mfma_kernel(const DecodeArgs a) {
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
       u32x4 w = {0u, 0u, 0u, 0u};
-      if (g < G) w = ld16(qrow + q_col<FP8, D>(kk, q4));
+      if (g < G) w = ld16(qrow + q_col<KF, D>(kk, q4));
       qB[kk] = __builtin_bit_cast(bf16x8, w);
     }
   }
 
   // Wave w of a KV head takes the partition's tiles w, w + W, w + 2W, ... (PT of them).
   auto load_k = [&](int i) {
-    KTile<FP8, D> t;
+    KTile<KF, D> t;
     const int tok = t0 + 16 * (i * W + w) + n;
     const uint8_t* p;
     if constexpr (BIGBS) p = kbase + tile_block(i) + lane_row(tok) + 16 * q4;
     else p = kbase + row_off(tok) + 16 * q4;
 #pragma unroll
-    for (int j = 0; j < KTile<FP8, D>::N; ++j) {
+    for (int j = 0; j < KTile<KF, D>::N; ++j) {
       if constexpr (PA_NT_K) t.w[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p + 64 * j));
       else t.w[j] = ld16(p + 64 * j);
     }
     return t;
   };
   auto load_v = [&](int i) {
-    VTile<FP8, D> t;
+    VTile<KF, D> t;
     int64_t tb = 0;
     if constexpr (BIGBS) tb = tile_block(i);
 #pragma unroll
@@ -195,8 +195,8 @@ void decode_mfma_kernel(const DecodeArgs a) {
       const uint8_t* p;
       if constexpr (BIGBS) p = vbase + tb + lane_row(tok) + n * VEC * ESZ;
       else p = vbase + row_off(tok) + n * VEC * ESZ;
-      if constexpr (PA_NT_V) t.w[j] = __builtin_nontemporal_load(reinterpret_cast<const typename VTile<FP8, D>::W*>(p));
-      else t.w[j] = *reinterpret_cast<const typename VTile<FP8, D>::W*>(p);
+      if constexpr (PA_NT_V) t.w[j] = __builtin_nontemporal_load(reinterpret_cast<const typename VTile<KF, D>::W*>(p));
+      else t.w[j] = *reinterpret_cast<const typename VTile<KF, D>::W*>(p);
     }
     return t;
   };
@@ -205,16 +205,16 @@ void decode_mfma_kernel(const DecodeArgs a) {
   // The ring runs on into V: as the last K tiles are consumed, the first V tiles
   // are already requested, so the stream of loads does not pause between phases.
   float S[PT][4];
-  KTile<FP8, D> kt[KD];
-  VTile<FP8, D> vt[KD];
+  KTile<KF, D> kt[KD];
+  VTile<KF, D> vt[KD];
 #pragma unroll
   for (int i = 0; i < KD; ++i) kt[i] = load_k(i);
 #pragma unroll
   for (int i = 0; i < PT; ++i) {
-    const KTile<FP8, D> cur = kt[i % KD];
+    const KTile<KF, D> cur = kt[i % KD];
     if (i + KD < PT) kt[i % KD] = load_k(i + KD);
     else vt[i + KD - PT] = load_v(i + KD - PT);
-    const f32x4 s = qk_tile<FP8, D>(cur, qB);
+    const f32x4 s = qk_tile<KF, D>(cur, qB);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int tok = t0 + 16 * (i * W + w) + 4 * q4 + r;
@@ -255,9 +255,9 @@ void decode_mfma_kernel(const DecodeArgs a) {
   for (int e = 0; e < VEC; ++e) O[e] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int i = 0; i < PT; ++i) {
-    const VTile<FP8, D> cur = vt[i % KD];
+    const VTile<KF, D> cur = vt[i % KD];
     if (i + KD < PT) vt[i % KD] = load_v(i + KD);
-    pv_tile<FP8, D>(cur, Pk[i][0], Pk[i][1], O);
+    pv_tile<KF, D>(cur, Pk[i][0], Pk[i][1], O);
   }
 
   // ---- combine the W waves of each KV head (W > 1) --------------------------------
@@ -358,32 +358,36 @@ void decode_mfma_kernel(const DecodeArgs a) {
   }
 }
 
-template <bool FP8, int D, bool BIGBS>
+template <int KF, int D, bool BIGBS>
 static hipError_t launch_pt(const DecodeArgs& a, dim3 grid, dim3 block, hipStream_t s) {
   const size_t lds = a.waves_per_head > 1 ? sizeof(float) * combine_floats(a.waves_per_head) * a.heads_per_wg : 0;
   switch (a.partition_tokens / a.waves_per_head) {
-    case 16: hipLaunchKernelGGL((decode_mfma_kernel<FP8, D, 1, BIGBS>), grid, block, lds, s, a); break;
-    case 32: hipLaunchKernelGGL((decode_mfma_kernel<FP8, D, 2, BIGBS>), grid, block, lds, s, a); break;
-    case 64: hipLaunchKernelGGL((decode_mfma_kernel<FP8, D, 4, BIGBS>), grid, block, lds, s, a); break;
-    case 128: hipLaunchKernelGGL((decode_mfma_kernel<FP8, D, 8, BIGBS>), grid, block, lds, s, a); break;
-    case 256: hipLaunchKernelGGL((decode_mfma_kernel<FP8, D, 16, BIGBS>), grid, block, lds, s, a); break;
+    case 16: hipLaunchKernelGGL((decode_mfma_kernel<KF, D, 1, BIGBS>), grid, block, lds, s, a); break;
+    case 32: hipLaunchKernelGGL((decode_mfma_kernel<KF, D, 2, BIGBS>), grid, block, lds, s, a); break;
+    case 64: hipLaunchKernelGGL((decode_mfma_kernel<KF, D, 4, BIGBS>), grid, block, lds, s, a); break;
+    case 128: hipLaunchKernelGGL((decode_mfma_kernel<KF, D, 8, BIGBS>), grid, block, lds, s, a); break;
+    case 256: hipLaunchKernelGGL((decode_mfma_kernel<KF, D, 16, BIGBS>), grid, block, lds, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
-template <bool FP8, int D>
+template <int KF, int D>
 static hipError_t launch_bs(const DecodeArgs& a, dim3 grid, dim3 block, hipStream_t s) {
-  return a.block_size >= 16 ? launch_pt<FP8, D, true>(a, grid, block, s) : launch_pt<FP8, D, false>(a, grid, block, s);
+  return a.block_size >= 16 ? launch_pt<KF, D, true>(a, grid, block, s) : launch_pt<KF, D, false>(a, grid, block, s);
 }
 
 hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t s) {
   const dim3 grid = a.dense ? dim3((unsigned)(a.max_parts * a.head_groups * a.num_seqs), 1u)
                            : dim3((unsigned)(a.max_parts * a.head_groups), (unsigned)a.num_seqs);
   const dim3 block((unsigned)(kWave * a.heads_per_wg * a.waves_per_head));
-  const bool fp8 = a.kv_fmt == kE4m3;
-  if (a.head_dim == 128) return fp8 ? launch_bs<true, 128>(a, grid, block, s) : launch_bs<false, 128>(a, grid, block, s);
-  return fp8 ? launch_bs<true, 64>(a, grid, block, s) : launch_bs<false, 64>(a, grid, block, s);
+  const bool d128 = a.head_dim == 128;
+  switch (a.kv_fmt) {
+    case kBf16: return d128 ? launch_bs<kFmtBf16, 128>(a, grid, block, s) : launch_bs<kFmtBf16, 64>(a, grid, block, s);
+    case kE4m3: return d128 ? launch_bs<kFmtE4m3, 128>(a, grid, block, s) : launch_bs<kFmtE4m3, 64>(a, grid, block, s);
+    case kInt8: return d128 ? launch_bs<kFmtInt8, 128>(a, grid, block, s) : launch_bs<kFmtInt8, 64>(a, grid, block, s);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace pa

@@ -28,18 +28,18 @@
 
 namespace pa {
 
-template <bool FP8, int D, int PT, bool BIGBS>
+template <int KF, int D, int PT, bool BIGBS>
 __global__ __launch_bounds__(256) void decode_persist_kernel(const DecodeArgs a) {
   constexpr int P = 16 * PT;
-  constexpr int ESZ = FP8 ? 1 : 2;
+  constexpr int ESZ = byte_fmt(KF) ? 1 : 2;
   constexpr int VEC = D / 16;
   constexpr int NKK = D / 32;
   constexpr int NSTEP = 2 * PT;
   constexpr int DEPTH = NSTEP < PA_PERSIST_DEPTH ? NSTEP : PA_PERSIST_DEPTH;
   static_assert(NSTEP % DEPTH == 0, "ring depth must divide the steps of a unit");
   constexpr int NR = BIGBS ? 1 : (P + 63) / 64;   // block-table registers per lane
-  using KT = KTile<FP8, D>;
-  using VT = VTile<FP8, D>;
+  using KT = KTile<KF, D>;
+  using VT = VTile<KF, D>;
   static_assert(sizeof(KT) == sizeof(VT), "K and V tiles share ring slots");
   struct Slot { uint32_t w[sizeof(KT) / 4]; };
 
@@ -124,7 +124,7 @@ __global__ __launch_bounds__(256) void decode_persist_kernel(const DecodeArgs a)
                            ((int64_t)r.b * a.num_q_heads + r.kvh * G + min(n, G - 1)) * D;
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
-      u32x4 w = ld16(qrow + q_col<FP8, D>(kk, q4));
+      u32x4 w = ld16(qrow + q_col<KF, D>(kk, q4));
       if (n >= G) w = u32x4{0u, 0u, 0u, 0u};
       qv[kk] = __builtin_bit_cast(bf16x8, w);
     }
@@ -260,7 +260,7 @@ __global__ __launch_bounds__(256) void decode_persist_kernel(const DecodeArgs a)
         ring[s % DEPTH] = t < NSTEP ? issue(t, cur, tb) : issue(t - NSTEP, nxt, tb_n);
 
         if (s < PT) {                                    // logits of tile s, base 2, masked
-          const f32x4 sc = qk_tile<FP8, D>(__builtin_bit_cast(KT, data), qB);
+          const f32x4 sc = qk_tile<KF, D>(__builtin_bit_cast(KT, data), qB);
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int tok = t0 + 16 * s + 4 * q4 + r;
@@ -290,7 +290,7 @@ __global__ __launch_bounds__(256) void decode_persist_kernel(const DecodeArgs a)
           lsum += __shfl_xor(lsum, 16);
           lsum += __shfl_xor(lsum, 32);
         }
-        if (s >= PT) pv_tile<FP8, D>(__builtin_bit_cast(VT, data), Pk[s - PT][0], Pk[s - PT][1], O);
+        if (s >= PT) pv_tile<KF, D>(__builtin_bit_cast(VT, data), Pk[s - PT][0], Pk[s - PT][1], O);
       }
 
       finalize(cur, O, mx, lsum);
@@ -308,10 +308,10 @@ __global__ __launch_bounds__(256) void decode_persist_kernel(const DecodeArgs a)
 
 }
 
-template <bool FP8, int D, int PT>
+template <int KF, int D, int PT>
 static hipError_t launch_bs(const DecodeArgs& a, hipStream_t s) {
-  const void* fn = a.block_size >= 16 ? reinterpret_cast<const void*>(&decode_persist_kernel<FP8, D, PT, true>)
-                                      : reinterpret_cast<const void*>(&decode_persist_kernel<FP8, D, PT, false>);
+  const void* fn = a.block_size >= 16 ? reinterpret_cast<const void*>(&decode_persist_kernel<KF, D, PT, true>)
+                                      : reinterpret_cast<const void*>(&decode_persist_kernel<KF, D, PT, false>);
   int dev = 0, cus = 0, per_cu = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
@@ -319,28 +319,32 @@ static hipError_t launch_bs(const DecodeArgs& a, hipStream_t s) {
   if (e != hipSuccess) return e;
   const int grid = max(1, cus * max(1, per_cu));
   if (a.block_size >= 16)
-    hipLaunchKernelGGL((decode_persist_kernel<FP8, D, PT, true>), dim3(grid), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((decode_persist_kernel<KF, D, PT, true>), dim3(grid), dim3(256), 0, s, a);
   else
-    hipLaunchKernelGGL((decode_persist_kernel<FP8, D, PT, false>), dim3(grid), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((decode_persist_kernel<KF, D, PT, false>), dim3(grid), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
-template <bool FP8, int D>
+template <int KF, int D>
 static hipError_t launch_pt(const DecodeArgs& a, hipStream_t s) {
   switch (a.partition_tokens) {
-    case 16: return launch_bs<FP8, D, 1>(a, s);
-    case 32: return launch_bs<FP8, D, 2>(a, s);
-    case 64: return launch_bs<FP8, D, 4>(a, s);
-    case 128: return launch_bs<FP8, D, 8>(a, s);
-    case 256: return launch_bs<FP8, D, 16>(a, s);
+    case 16: return launch_bs<KF, D, 1>(a, s);
+    case 32: return launch_bs<KF, D, 2>(a, s);
+    case 64: return launch_bs<KF, D, 4>(a, s);
+    case 128: return launch_bs<KF, D, 8>(a, s);
+    case 256: return launch_bs<KF, D, 16>(a, s);
     default: return hipErrorInvalidValue;
   }
 }
 
 hipError_t launch_decode_persist(const DecodeArgs& a, hipStream_t s) {
-  const bool fp8 = a.kv_fmt == kE4m3;
-  if (a.head_dim == 128) return fp8 ? launch_pt<true, 128>(a, s) : launch_pt<false, 128>(a, s);
-  return fp8 ? launch_pt<true, 64>(a, s) : launch_pt<false, 64>(a, s);
+  const bool d128 = a.head_dim == 128;
+  switch (a.kv_fmt) {
+    case kBf16: return d128 ? launch_pt<kFmtBf16, 128>(a, s) : launch_pt<kFmtBf16, 64>(a, s);
+    case kE4m3: return d128 ? launch_pt<kFmtE4m3, 128>(a, s) : launch_pt<kFmtE4m3, 64>(a, s);
+    case kInt8: return d128 ? launch_pt<kFmtInt8, 128>(a, s) : launch_pt<kFmtInt8, 64>(a, s);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace pa

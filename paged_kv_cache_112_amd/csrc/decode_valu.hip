@@ -49,6 +49,16 @@ struct Row<kE4m3> {
   }
 };
 
+template <>
+struct Row<kInt8> {
+  static constexpr int E = 8, BYTES = 8;
+  __device__ static void load(const uint8_t* p, float* x) {
+    const u32x2 w = ld8(p);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) x[i] = (float)(int8_t)(w[i >> 2] >> (8 * (i & 3)));
+  }
+};
+
 template <int KVF, int QF, int D, int GMAX>
 __global__ __launch_bounds__(256) void decode_valu_kernel(const DecodeArgs a) {
   constexpr int ESZ = KVF == kF32 ? 4 : KVF == kBf16 ? 2 : 1;
@@ -232,6 +242,7 @@ hipError_t launch_decode_valu(const DecodeArgs& a, hipStream_t s) {
   if (a.kv_fmt == kF32 && a.q_fmt == kF32) return launch_d<kF32, kF32>(a, grid, block, s);
   if (a.kv_fmt == kBf16 && a.q_fmt == kBf16) return launch_d<kBf16, kBf16>(a, grid, block, s);
   if (a.kv_fmt == kE4m3 && a.q_fmt == kBf16) return launch_d<kE4m3, kBf16>(a, grid, block, s);
+  if (a.kv_fmt == kInt8 && a.q_fmt == kBf16) return launch_d<kInt8, kBf16>(a, grid, block, s);
   return hipErrorInvalidValue;
 }
 

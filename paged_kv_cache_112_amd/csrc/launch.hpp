@@ -14,12 +14,12 @@ struct WriteArgs {
   void* v_cache;
   int32_t num_tokens;
   int32_t row_elems;   // H_kv * head_dim
-  int32_t mode;        // 0 bf16 copy, 1 f32 copy, 2 bf16 -> e4m3, 3 f32 -> e4m3
-  float inv_k, inv_v;  // fp32(1 / scale) for e4m3 pools
+  int32_t mode;        // 0 bf16 copy, 1 f32 copy, 2 bf16 -> e4m3, 3 f32 -> e4m3, 4 bf16 -> int8, 5 f32 -> int8
+  float inv_k, inv_v;  // fp32(1 / scale) for e4m3 and int8 pools
 };
 
 // Storage formats, numbered as pa_dtype in include/pa.h.
-enum Fmt : int32_t { kF32 = 0, kBf16 = 1, kE4m3 = 2 };
+enum Fmt : int32_t { kF32 = 0, kBf16 = 1, kE4m3 = 2, kInt8 = 3 };
 
 struct DecodeArgs {
   const void* q;             // [B, H_q, D]

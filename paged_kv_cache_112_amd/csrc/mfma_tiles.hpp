@@ -14,23 +14,45 @@
 
 namespace pa {
 
-template <bool FP8, int D>
+// Pool element formats on the matrix-core path (numbered as pa_dtype): bf16 rows go to
+// the matrix cores as they are; one-byte formats (e4m3, int8) are widened to bf16 in
+// registers, exactly (every e4m3 value and every int8 value is a bf16 value).
+constexpr int kFmtBf16 = 1, kFmtE4m3 = 2, kFmtInt8 = 3;
+constexpr bool byte_fmt(int KF) { return KF != kFmtBf16; }
+
+// Two signed bytes of w (bytes 0, 1 or, with hi, bytes 2, 3) to a bf16 pair.  The
+// bytes are offset to unsigned (x ^ 0x80 = x + 128), converted exactly, and the offset
+// taken back off; |x| <= 128 has at most 8 significant bits, so the bf16 is exact.
+__device__ __forceinline__ uint32_t i8x2_to_bf16x2(uint32_t w, bool hi) {
+  const uint32_t u = (w ^ 0x80808080u) >> (hi ? 16 : 0);
+  const float a = (float)(u & 0xffu) - 128.0f;
+  const float b = (float)((u >> 8) & 0xffu) - 128.0f;
+  return pack_hi_halves(__float_as_uint(a), __float_as_uint(b));
+}
+
+template <int KF>
+__device__ __forceinline__ uint32_t bytes2_to_bf16x2(uint32_t w, bool hi) {
+  if constexpr (KF == kFmtInt8) return i8x2_to_bf16x2(w, hi);
+  else return e4m3x2_to_bf16x2(hi ? e4m3x2_hi(w) : e4m3x2_lo(w));
+}
+
+template <int KF, int D>
 struct KTile {
-  static constexpr int N = FP8 ? D / 64 : D / 32;   // 16-byte loads per lane
+  static constexpr int N = byte_fmt(KF) ? D / 64 : D / 32;   // 16-byte loads per lane
   u32x4 w[N];
 };
 
-template <bool FP8, int D>
+template <int KF, int D>
 struct VTile {
   // bytes per lane per row: VEC elements, VEC = D / 16
-  static constexpr int BYTES = (D / 16) * (FP8 ? 1 : 2);
+  static constexpr int BYTES = (D / 16) * (byte_fmt(KF) ? 1 : 2);
   typedef typename std::conditional<BYTES == 16, u32x4, typename std::conditional<BYTES == 8, u32x2, uint32_t>::type>::type W;
   W w[4];
 };
 
-template <bool FP8, int D>
+template <int KF, int D>
 __device__ __forceinline__ int q_col(int kk, int q4) {
-  if constexpr (FP8) {
+  if constexpr (byte_fmt(KF)) {
     if constexpr (D == 128) return 64 * (kk >> 1) + 16 * q4 + 8 * (kk & 1);
     else return 16 * q4 + 8 * kk;
   } else {
@@ -38,30 +60,31 @@ __device__ __forceinline__ int q_col(int kk, int q4) {
   }
 }
 
-// Eight E4M3 bytes (two words) to a bf16x8 MFMA operand, element order preserved.
-__device__ __forceinline__ bf16x8 e4m3x8_to_bf16x8(uint32_t w0, uint32_t w1) {
+// Eight one-byte elements (two words) to a bf16x8 MFMA operand, element order preserved.
+template <int KF>
+__device__ __forceinline__ bf16x8 bytes8_to_bf16x8(uint32_t w0, uint32_t w1) {
   u32x4 r;
-  r[0] = e4m3x2_to_bf16x2(e4m3x2_lo(w0));
-  r[1] = e4m3x2_to_bf16x2(e4m3x2_hi(w0));
-  r[2] = e4m3x2_to_bf16x2(e4m3x2_lo(w1));
-  r[3] = e4m3x2_to_bf16x2(e4m3x2_hi(w1));
+  r[0] = bytes2_to_bf16x2<KF>(w0, false);
+  r[1] = bytes2_to_bf16x2<KF>(w0, true);
+  r[2] = bytes2_to_bf16x2<KF>(w1, false);
+  r[3] = bytes2_to_bf16x2<KF>(w1, true);
   return __builtin_bit_cast(bf16x8, r);
 }
 
 // Raw q.K^T of one tile: lane (g = n, q4) gets dot(q_g, K_t) for tokens t = 4*q4 + r in
 // register r (the C layout of the 16x16 product with m = token, n = query head).
-template <bool FP8, int D>
-__device__ __forceinline__ f32x4 qk_tile(const KTile<FP8, D>& k, const bf16x8 (&qB)[D / 32]) {
+template <int KF, int D>
+__device__ __forceinline__ f32x4 qk_tile(const KTile<KF, D>& k, const bf16x8 (&qB)[D / 32]) {
   f32x4 s = {0.f, 0.f, 0.f, 0.f};
-  if constexpr (!FP8) {
+  if constexpr (!byte_fmt(KF)) {
 #pragma unroll
     for (int kk = 0; kk < D / 32; ++kk)
       s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, k.w[kk]), qB[kk], s, 0, 0, 0);
   } else {
 #pragma unroll
-    for (int h = 0; h < KTile<FP8, D>::N; ++h) {
-      s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(e4m3x8_to_bf16x8(k.w[h][0], k.w[h][1]), qB[2 * h], s, 0, 0, 0);
-      s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(e4m3x8_to_bf16x8(k.w[h][2], k.w[h][3]), qB[2 * h + 1], s, 0, 0, 0);
+    for (int h = 0; h < KTile<KF, D>::N; ++h) {
+      s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bytes8_to_bf16x8<KF>(k.w[h][0], k.w[h][1]), qB[2 * h], s, 0, 0, 0);
+      s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bytes8_to_bf16x8<KF>(k.w[h][2], k.w[h][3]), qB[2 * h + 1], s, 0, 0, 0);
     }
   }
   return s;
@@ -72,24 +95,24 @@ __device__ __forceinline__ f32x4 qk_tile(const KTile<FP8, D>& k, const bf16x8 (&
 // of v_mfma_f32_16x16x16_bf16.  The V rows are re-paired into token-major B
 // operands (k = token, n = column), one product per column offset e < VEC;
 // O[e] then holds O[g = 4*q4' + r][VEC*n + e] in lane (n, q4'), register r.
-template <bool FP8, int D>
-__device__ __forceinline__ void pv_tile(const VTile<FP8, D>& v, uint32_t p01, uint32_t p23, f32x4 (&O)[D / 16]) {
+template <int KF, int D>
+__device__ __forceinline__ void pv_tile(const VTile<KF, D>& v, uint32_t p01, uint32_t p23, f32x4 (&O)[D / 16]) {
   constexpr int VEC = D / 16;
   const bf16x4 A = __builtin_bit_cast(bf16x4, u32x2{p01, p23});
   uint32_t rw[4][VEC / 2];                  // per token row: bf16 pairs (columns 2c, 2c+1)
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    if constexpr (!FP8) {
+    if constexpr (!byte_fmt(KF)) {
 #pragma unroll
       for (int c = 0; c < VEC / 2; ++c) rw[j][c] = v.w[j][c];
     } else if constexpr (VEC == 8) {
-      rw[j][0] = e4m3x2_to_bf16x2(e4m3x2_lo(v.w[j][0]));
-      rw[j][1] = e4m3x2_to_bf16x2(e4m3x2_hi(v.w[j][0]));
-      rw[j][2] = e4m3x2_to_bf16x2(e4m3x2_lo(v.w[j][1]));
-      rw[j][3] = e4m3x2_to_bf16x2(e4m3x2_hi(v.w[j][1]));
+      rw[j][0] = bytes2_to_bf16x2<KF>(v.w[j][0], false);
+      rw[j][1] = bytes2_to_bf16x2<KF>(v.w[j][0], true);
+      rw[j][2] = bytes2_to_bf16x2<KF>(v.w[j][1], false);
+      rw[j][3] = bytes2_to_bf16x2<KF>(v.w[j][1], true);
     } else {
-      rw[j][0] = e4m3x2_to_bf16x2(e4m3x2_lo(v.w[j]));
-      rw[j][1] = e4m3x2_to_bf16x2(e4m3x2_hi(v.w[j]));
+      rw[j][0] = bytes2_to_bf16x2<KF>(v.w[j], false);
+      rw[j][1] = bytes2_to_bf16x2<KF>(v.w[j], true);
     }
   }
 #pragma unroll
@@ -107,24 +130,24 @@ __device__ __forceinline__ void pv_tile(const VTile<FP8, D>& v, uint32_t p01, ui
 // column VEC*n + e of its four V rows.  Afterwards lane (n', q4') register r of O[e]
 // holds O[head n'][d = VEC*(4*q4' + r) + e]: every lane keeps its own head's values,
 // so a per-head rescale is a lane-local multiply.
-template <bool FP8, int D>
-__device__ __forceinline__ void pvt_tile(const VTile<FP8, D>& v, uint32_t p01, uint32_t p23, f32x4 (&O)[D / 16]) {
+template <int KF, int D>
+__device__ __forceinline__ void pvt_tile(const VTile<KF, D>& v, uint32_t p01, uint32_t p23, f32x4 (&O)[D / 16]) {
   constexpr int VEC = D / 16;
   const bf16x4 B = __builtin_bit_cast(bf16x4, u32x2{p01, p23});
   uint32_t rw[4][VEC / 2];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    if constexpr (!FP8) {
+    if constexpr (!byte_fmt(KF)) {
 #pragma unroll
       for (int c = 0; c < VEC / 2; ++c) rw[j][c] = v.w[j][c];
     } else if constexpr (VEC == 8) {
-      rw[j][0] = e4m3x2_to_bf16x2(e4m3x2_lo(v.w[j][0]));
-      rw[j][1] = e4m3x2_to_bf16x2(e4m3x2_hi(v.w[j][0]));
-      rw[j][2] = e4m3x2_to_bf16x2(e4m3x2_lo(v.w[j][1]));
-      rw[j][3] = e4m3x2_to_bf16x2(e4m3x2_hi(v.w[j][1]));
+      rw[j][0] = bytes2_to_bf16x2<KF>(v.w[j][0], false);
+      rw[j][1] = bytes2_to_bf16x2<KF>(v.w[j][0], true);
+      rw[j][2] = bytes2_to_bf16x2<KF>(v.w[j][1], false);
+      rw[j][3] = bytes2_to_bf16x2<KF>(v.w[j][1], true);
     } else {
-      rw[j][0] = e4m3x2_to_bf16x2(e4m3x2_lo(v.w[j]));
-      rw[j][1] = e4m3x2_to_bf16x2(e4m3x2_hi(v.w[j]));
+      rw[j][0] = bytes2_to_bf16x2<KF>(v.w[j], false);
+      rw[j][1] = bytes2_to_bf16x2<KF>(v.w[j], true);
     }
   }
 #pragma unroll

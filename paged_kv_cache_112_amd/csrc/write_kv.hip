@@ -12,7 +12,14 @@
 
 namespace pa {
 
-enum class WriteMode { kCopy16, kCopy32, kBf16ToE4m3, kF32ToE4m3 };
+enum class WriteMode { kCopy16, kCopy32, kBf16ToE4m3, kF32ToE4m3, kBf16ToInt8, kF32ToInt8 };
+
+// Round to a symmetric int8 code: nearest, ties to even, saturating to +-127; NaN -> 0.
+__device__ __forceinline__ uint32_t f32_to_i8(float y) {
+  if (y != y) return 0u;
+  const float r = fminf(fmaxf(__builtin_rintf(y), -127.0f), 127.0f);
+  return (uint32_t)(int32_t)r & 0xffu;
+}
 
 template <WriteMode M>
 __global__ __launch_bounds__(256) void write_kv_kernel(const uint8_t* __restrict__ k, const uint8_t* __restrict__ v,
@@ -39,7 +46,7 @@ __global__ __launch_bounds__(256) void write_kv_kernel(const uint8_t* __restrict
     st16(vc + dst_elem * 4 + 16, v1);
   } else {
     float xk[8], xv[8];
-    if constexpr (M == WriteMode::kBf16ToE4m3) {
+    if constexpr (M == WriteMode::kBf16ToE4m3 || M == WriteMode::kBf16ToInt8) {
       const u32x4 a = ld16(k + src_elem * 2), b = ld16(v + src_elem * 2);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -58,9 +65,14 @@ __global__ __launch_bounds__(256) void write_kv_kernel(const uint8_t* __restrict
     u32x2 ok = {0u, 0u}, ov = {0u, 0u};
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      // one fp32 multiply, then round to E4M3 (no fused multiply-add is possible here)
-      ok[i >> 2] |= f32_to_e4m3(xk[i] * inv_k) << (8 * (i & 3));
-      ov[i >> 2] |= f32_to_e4m3(xv[i] * inv_v) << (8 * (i & 3));
+      // one fp32 multiply, then round to the one-byte code (no fused multiply-add is possible here)
+      if constexpr (M == WriteMode::kBf16ToE4m3 || M == WriteMode::kF32ToE4m3) {
+        ok[i >> 2] |= f32_to_e4m3(xk[i] * inv_k) << (8 * (i & 3));
+        ov[i >> 2] |= f32_to_e4m3(xv[i] * inv_v) << (8 * (i & 3));
+      } else {
+        ok[i >> 2] |= f32_to_i8(xk[i] * inv_k) << (8 * (i & 3));
+        ov[i >> 2] |= f32_to_i8(xv[i] * inv_v) << (8 * (i & 3));
+      }
     }
     st8(kc + dst_elem, ok);
     st8(vc + dst_elem, ov);
@@ -84,7 +96,11 @@ hipError_t launch_write_kv(const WriteArgs& a, hipStream_t stream) {
                                total, cpr, a.inv_k, a.inv_v); break;
     case 2: hipLaunchKernelGGL(write_kv_kernel<WriteMode::kBf16ToE4m3>, grid, block, 0, stream, k, v, a.slots, kc,
                                vc, total, cpr, a.inv_k, a.inv_v); break;
-    default: hipLaunchKernelGGL(write_kv_kernel<WriteMode::kF32ToE4m3>, grid, block, 0, stream, k, v, a.slots, kc,
+    case 3: hipLaunchKernelGGL(write_kv_kernel<WriteMode::kF32ToE4m3>, grid, block, 0, stream, k, v, a.slots, kc,
+                               vc, total, cpr, a.inv_k, a.inv_v); break;
+    case 4: hipLaunchKernelGGL(write_kv_kernel<WriteMode::kBf16ToInt8>, grid, block, 0, stream, k, v, a.slots, kc,
+                               vc, total, cpr, a.inv_k, a.inv_v); break;
+    default: hipLaunchKernelGGL(write_kv_kernel<WriteMode::kF32ToInt8>, grid, block, 0, stream, k, v, a.slots, kc,
                                 vc, total, cpr, a.inv_k, a.inv_v); break;
   }
   return hipGetLastError();

@@ -12,8 +12,9 @@ import numpy as np
 import oracle
 from workloads import DecodeWorkload, f32_to_bf16_bits
 
-STORAGE = {"f32": np.float32, "bf16": np.uint16, "e4m3": np.uint8}
-POISON = {"f32": np.float32(np.nan), "bf16": np.uint16(0x7FC0), "e4m3": np.uint8(0x7F)}
+STORAGE = {"f32": np.float32, "bf16": np.uint16, "e4m3": np.uint8, "i8": np.int8}
+# int8 has no NaN: -128 is a code the symmetric quantizer never writes
+POISON = {"f32": np.float32(np.nan), "bf16": np.uint16(0x7FC0), "e4m3": np.uint8(0x7F), "i8": np.int8(-128)}
 
 
 class HostInputs:
@@ -37,15 +38,16 @@ def _encode_input(x_f32: np.ndarray, w: DecodeWorkload):
     return f32_to_bf16_bits(x_f32), "bf16"
 
 
-def fp8_scales(w: DecodeWorkload):
-    """Per-pool scale = fp32(amax / 448) over every value written (bf16-rounded first)."""
+def fp8_scales(w: DecodeWorkload, qmax: float = 448.0):
+    """Per-pool scale = fp32(amax / qmax) over every value written (bf16-rounded first):
+    448 for e4m3, 127 for int8."""
     amax = [0.0, 0.0]
     for b in range(w.num_seqs):
         for i, which in enumerate("kv"):
             x, _ = _encode_input(w.seq_token_values(which, b), w)
             vals = (x.astype(np.uint32) << 16).view(np.float32)
             amax[i] = max(amax[i], float(np.abs(vals).max(initial=0.0)))
-    return float(np.float32(amax[0] / 448.0)), float(np.float32(amax[1] / 448.0))
+    return float(np.float32(amax[0] / qmax)), float(np.float32(amax[1] / qmax))
 
 
 def build_host_inputs(w: DecodeWorkload, skip_last: bool = False) -> HostInputs:
@@ -54,7 +56,7 @@ def build_host_inputs(w: DecodeWorkload, skip_last: bool = False) -> HostInputs:
     shape = (w.num_blocks, w.block_size, w.num_kv_heads, w.head_dim)
     kc = np.full(shape, POISON[fmt], dtype=STORAGE[fmt])
     vc = np.full(shape, POISON[fmt], dtype=STORAGE[fmt])
-    ks, vs = fp8_scales(w) if fmt == "e4m3" else (1.0, 1.0)
+    ks, vs = fp8_scales(w) if fmt == "e4m3" else fp8_scales(w, 127.0) if fmt == "i8" else (1.0, 1.0)
     for b in range(w.num_seqs):
         pos = w.owned_positions(b)
         K, kin = _encode_input(w.seq_token_values("k", b), w)

@@ -36,10 +36,11 @@ class MQ:
         self.ks = self.vs = 1.0
         kvals = [rng.standard_normal((int(s), hkv, d)).astype(np.float32) for s in seq_lens]
         vvals = [rng.standard_normal((int(s), hkv, d)).astype(np.float32) for s in seq_lens]
-        if kv == "e4m3":
+        if kv in ("e4m3", "i8"):
+            qmax = 448.0 if kv == "e4m3" else 127.0
             bf = lambda x: (f32_to_bf16_bits(x).astype(np.uint32) << 16).view(np.float32)
-            self.ks = float(np.float32(max(np.abs(bf(x)).max() for x in kvals) / 448))
-            self.vs = float(np.float32(max(np.abs(bf(x)).max() for x in vvals) / 448))
+            self.ks = float(np.float32(max(np.abs(bf(x)).max() for x in kvals) / qmax))
+            self.vs = float(np.float32(max(np.abs(bf(x)).max() for x in vvals) / qmax))
         for t, s, kk, vv in zip(tables, seq_lens, kvals, vvals):
             slots = [t[p // bs] * bs + p % bs for p in range(int(s))]
             oracle.write_kv(self.kc, self.vc, f32_to_bf16_bits(kk), f32_to_bf16_bits(vv), slots, kv, "bf16",
@@ -61,7 +62,7 @@ class MQ:
                                       "bf16", self.ks, self.vs, rows=rows)
 
 
-@pytest.mark.parametrize("kv", ["bf16", "e4m3"])
+@pytest.mark.parametrize("kv", ["bf16", "e4m3", "i8"])
 def test_printed_check(kv):
     """The page's check: decode 1 of 37, a full prefill of 5, the last 8 of 20; its block tables."""
     g = json.load(open(os.path.join(GOLDEN, "p2_round_robin_tables.json")))
@@ -81,7 +82,7 @@ def test_mixed_query_lengths(hq, hkv, d, bs):
     assert np.abs(out_to_f64(m.run(scale)) - m.oracle(scale)).max() <= 2e-2
 
 
-@pytest.mark.parametrize("kv", ["bf16", "e4m3"])
+@pytest.mark.parametrize("kv", ["bf16", "e4m3", "i8"])
 def test_peaky_scores(kv):
     """A large scale makes each row nearly one-hot: a wrong key or mask shows as an O(1) error."""
     m = MQ([70, 33, 129], [70, 9, 20], 32, 8, 128, 16, kv, seed=9)

@@ -72,3 +72,9 @@ def test_llama3_fp8_shared_prefix():
     out = _parity(dev, 2e-2)
     a = out_to_f64(dev.decode(kernel=1))
     assert np.abs(a - out).max() <= 2e-2
+
+
+def test_llama3_b64_int8_pool():
+    """The batch-64 workload with int8 pools (symmetric, per-pool scale amax / 127)."""
+    w = make_config("llama3_8b_b64").with_dtypes("i8", "bf16")
+    _parity(DeviceInputs(build_host_inputs(w)), 2e-2)

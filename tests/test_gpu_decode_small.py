@@ -12,7 +12,7 @@ from workloads import make_config
 
 pytestmark = pytest.mark.gpu
 
-TOL = {"f32": 1e-5, "bf16": 2e-2, "e4m3": 2e-2}
+TOL = {"f32": 1e-5, "bf16": 2e-2, "e4m3": 2e-2, "i8": 2e-2}
 KERNELS = {"valu": 1, "mfma": 2, "persist": 3}
 
 
@@ -59,7 +59,8 @@ EDGE_CTX = [1, 2, 15, 16, 17, 31, 255, 256, 257, 300, 511, 513, 0, 64]
 
 @pytest.mark.parametrize("kv,q,kernel", [("f32", "f32", "valu"), ("bf16", "bf16", "mfma"), ("bf16", "bf16", "valu"),
                                          ("bf16", "bf16", "persist"), ("e4m3", "bf16", "mfma"), ("e4m3", "bf16", "valu"),
-                                         ("e4m3", "bf16", "persist")])
+                                         ("e4m3", "bf16", "persist"), ("i8", "bf16", "mfma"), ("i8", "bf16", "valu"),
+                                         ("i8", "bf16", "persist")])
 @pytest.mark.parametrize("hq,hkv,d", [(32, 8, 128), (8, 8, 64), (16, 2, 128)])
 @pytest.mark.parametrize("P", [0, 64])
 def test_edge_lengths(kv, q, kernel, hq, hkv, d, P):
@@ -68,7 +69,8 @@ def test_edge_lengths(kv, q, kernel, hq, hkv, d, P):
 
 
 @pytest.mark.parametrize("bs", [1, 2, 8, 64, 256])
-@pytest.mark.parametrize("kv,kernel", [("bf16", "mfma"), ("f32", "valu"), ("e4m3", "mfma"), ("bf16", "persist")])
+@pytest.mark.parametrize("kv,kernel", [("bf16", "mfma"), ("f32", "valu"), ("e4m3", "mfma"), ("bf16", "persist"),
+                                       ("i8", "mfma")])
 def test_block_sizes(bs, kv, kernel):
     w = custom_workload([300, 1, 47, 129], 8, 2, 128, bs, kv, "f32" if kv == "f32" else "bf16", seed=bs)
     _check(DeviceInputs(build_host_inputs(w)), w, partition_tokens=64, kernel=KERNELS[kernel])
@@ -78,7 +80,7 @@ def test_block_sizes(bs, kv, kernel):
 LONG_EDGE_CTX = EDGE_CTX + [767, 768, 769, 1023, 1024, 1025, 2047, 2048, 2049, 3000]
 
 
-@pytest.mark.parametrize("kv", ["bf16", "e4m3"])
+@pytest.mark.parametrize("kv", ["bf16", "e4m3", "i8"])
 @pytest.mark.parametrize("hq,hkv,d", [(32, 8, 128), (8, 8, 64), (16, 2, 128), (32, 2, 128)])
 @pytest.mark.parametrize("P", [512, 1024])
 def test_multi_wave_partitions(kv, hq, hkv, d, P):

@@ -86,3 +86,22 @@ def test_e4m3_write_from_f32():
     pool = np.full((64, 16, 8, 128), 0x7F, dtype=np.uint8)
     got_k, got_v, ref_k, ref_v = _run(pool, pool.copy(), x, -x, slots, "e4m3", "f32", 0.0625, 0.11)
     assert np.array_equal(got_k, ref_k) and np.array_equal(got_v, ref_v)
+
+
+@pytest.mark.parametrize("scale", [1.0, 0.5, float(np.float32(5.0 / 127)), float(np.float32(1 / 3))])
+def test_int8_write_all_bf16_patterns(scale):
+    """Every one of the 65,536 bf16 bit patterns quantized to int8 by the GPU write equals the oracle's code."""
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16).reshape(64, 8, 128)
+    slots = np.arange(64, dtype=np.int32)[::-1].copy()
+    pool = np.zeros((4, 16, 8, 128), dtype=np.int8)
+    got_k, got_v, ref_k, ref_v = _run(pool, pool.copy(), bits, bits[::-1].copy(), slots, "i8", "bf16", scale, scale)
+    assert np.array_equal(got_k, ref_k) and np.array_equal(got_v, ref_v)
+
+
+def test_int8_write_from_f32():
+    x = standard_normal_f32(11, (300, 8, 128)) * np.float32(40.0)
+    x[0, 0, :8] = [np.inf, -np.inf, np.nan, 1e-40, -1e-45, 2.5, -3.5, 0.5]
+    slots = np.random.default_rng(12).permutation(64 * 16)[:300].astype(np.int32)
+    pool = np.full((64, 16, 8, 128), -128, dtype=np.int8)
+    got_k, got_v, ref_k, ref_v = _run(pool, pool.copy(), x, -x, slots, "i8", "f32", 1.0, 0.11)
+    assert np.array_equal(got_k, ref_k) and np.array_equal(got_v, ref_v)

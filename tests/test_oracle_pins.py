@@ -412,3 +412,37 @@ def test_e4m3_quantize_all_bf16_inputs(scale):
     assert (got[inf & (x > 0)] == 0x7E).all() and (got[inf & (x < 0)] == 0xFE).all()
     nan = np.isnan(x)
     assert (got[nan] & 0x7F == 0x7F).all()
+
+
+def _rne_int(y: Fraction) -> int:
+    """Round a rational to the nearest integer, ties to even."""
+    fl = y.numerator // y.denominator
+    rem = y - fl
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and fl % 2 == 1):
+        fl += 1
+    return fl
+
+
+@pytest.mark.parametrize("scale", [1.0, 0.5, float(np.float32(5.0 / 127)), float(np.float32(3.7 / 127)),
+                                   float(np.float32(1 / 3))])
+def test_int8_quantize_all_bf16_inputs(scale):
+    """Symmetric int8: clamp(RNE(fp32(x * fp32(1/scale))), -127, 127), against exact rationals."""
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    x = (bits.astype(np.uint32) << 16).view(np.float32)
+    got = oracle.int8_quantize(x, scale)
+    inv = _fp_round(Fraction(1) / Fraction(scale), 23, -126)
+    finite = np.isfinite(x)
+    for i in np.nonzero(finite)[0]:
+        y = _fp_round(Fraction(float(x[i])) * inv, 23, -126)
+        if abs(y) > 2 ** 128:                     # the fp32 product overflows to infinity
+            want = 127 if y > 0 else -127
+        else:
+            want = max(-127, min(127, _rne_int(y)))
+        assert int(got[i]) == want, (hex(int(bits[i])), scale)
+    assert (got[np.isinf(x) & (x > 0)] == 127).all() and (got[np.isinf(x) & (x < 0)] == -127).all()
+    assert (got[np.isnan(x)] == 0).all()
+
+
+def test_int8_decode_is_code_times_scale():
+    codes = np.arange(-128, 128, dtype=np.int8)
+    assert np.array_equal(oracle.to_f64(codes, "i8", 0.25), np.arange(-128, 128) * 0.25)
