@@ -31,7 +31,8 @@ WORKLOAD = "llama3_8b_b64"
 HBM_PEAK_GBS = 8000.0
 LAYERS = 8
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_partition_llama3_8b_b64.traffic.json")
-KERNEL_SOURCES = ["paged_kv_cache_112_amd/csrc/decode_mfma.hip", "paged_kv_cache_112_amd/csrc/common.hpp"]
+KERNEL_SOURCES = ["paged_kv_cache_112_amd/csrc/decode_mfma.hip", "paged_kv_cache_112_amd/csrc/common.hpp",
+                  "paged_kv_cache_112_amd/csrc/mfma_tiles.hpp", "paged_kv_cache_112_amd/csrc/launch.hpp"]
 
 
 def algorithmic_bytes(w, kv_bytes=2, q_bytes=2, out_bytes=2, in_bytes=2):
@@ -369,7 +370,11 @@ def main():
     bt = to_dev(w.block_tables)
     ctx = to_dev(w.context_lens)
     max_ctx = int(w.context_lens.max())
-    pools = [(k0, v0)] + [(k0.clone(), v0.clone()) for _ in range(LAYERS - 1)]
+    # the layers' pools as one allocation per K and V, [LAYERS, num_blocks, bs, H_kv, d], used by layer view
+    k_all = k0.unsqueeze(0).repeat(LAYERS, 1, 1, 1, 1)
+    v_all = v0.unsqueeze(0).repeat(LAYERS, 1, 1, 1, 1)
+    del k0, v0
+    pools = [(k_all[l], v_all[l]) for l in range(LAYERS)]
     out = torch.empty((B, hq, d), dtype=torch.bfloat16, device=dev)
     P = args.partition or pa.pa_default_partition_tokens()
     ws = pa.new_workspace(B, hq, d, max_ctx, P, dev)

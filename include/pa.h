@@ -126,6 +126,20 @@ pa_status pa_write_kv(const void* k, const void* v, int32_t in_dtype, int32_t nu
 pa_status pa_copy_blocks(void* k_cache, void* v_cache, const pa_kv_cache* cache, const int32_t* src,
                          const int32_t* dst, int32_t num_pairs, void* stream);
 
+/* Multi-layer pools.  A model keeps one K and one V pool per layer (ai-infra-
+ * handbooks "Paged KV cache", "Implementation": KV storage is one pair of
+ * [num_blocks, block_size, H_kv, d_h] tensors per layer), all indexed by the same
+ * block tables.  Here they may live in one allocation each for K and V:
+ *   [num_layers, num_blocks, block_size, H_kv, d_h],
+ * layer l's pool starting num_blocks * block_size * H_kv * d_h elements after layer
+ * l - 1's; every per-layer call (pa_write_kv, pa_decode, ...) takes that layer's
+ * base address with the same pa_kv_cache.  A copy-on-write copy must move the block
+ * in every layer: pa_copy_blocks_layers does pa_copy_blocks for each of num_layers
+ * layers in one launch (arguments as pa_copy_blocks; cache describes one layer).
+ * Errors: as pa_copy_blocks, and PA_ERR_SHAPE for num_layers outside 1 .. 65535. */
+pa_status pa_copy_blocks_layers(void* k_cache, void* v_cache, const pa_kv_cache* cache, int32_t num_layers,
+                                const int32_t* src, const int32_t* dst, int32_t num_pairs, void* stream);
+
 /* Partition size (tokens) used when a call passes partition_tokens = 0. */
 int32_t pa_default_partition_tokens(void);
 

@@ -20,7 +20,7 @@ PA_F32, PA_BF16, PA_FP8_E4M3, PA_INT8 = 0, 1, 2, 3
 # pa_kernel
 PA_KERNEL_AUTO, PA_KERNEL_VALU, PA_KERNEL_MFMA, PA_KERNEL_MFMA_PERSIST = 0, 1, 2, 3
 
-EXPORTED = ("pa_write_kv", "pa_copy_blocks", "pa_paged_attention", "pa_slot_mapping", "pa_decode", "pa_decode_partition", "pa_merge",
+EXPORTED = ("pa_write_kv", "pa_copy_blocks", "pa_copy_blocks_layers", "pa_paged_attention", "pa_slot_mapping", "pa_decode", "pa_decode_partition", "pa_merge",
             "pa_decode_workspace_bytes", "pa_default_partition_tokens", "pa_status_str")
 
 
@@ -55,6 +55,8 @@ def lib() -> ctypes.CDLL:
         L.pa_write_kv.restype = ctypes.c_int
         L.pa_copy_blocks.argtypes = [_vp, _vp, ctypes.POINTER(PaKvCache), _vp, _vp, _i32, _vp]
         L.pa_copy_blocks.restype = ctypes.c_int
+        L.pa_copy_blocks_layers.argtypes = [_vp, _vp, ctypes.POINTER(PaKvCache), _i32, _vp, _vp, _i32, _vp]
+        L.pa_copy_blocks_layers.restype = ctypes.c_int
         L.pa_slot_mapping.argtypes = [_vp, _i32, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp]
         L.pa_slot_mapping.restype = ctypes.c_int
         L.pa_paged_attention.argtypes = [_vp, _i32, _i32, _i32, _i32, _vp, _vp, ctypes.POINTER(PaKvCache), _vp,
@@ -94,6 +96,11 @@ def pa_write_kv(k, v, in_dtype, num_tokens, slot_mapping, k_cache, v_cache, cach
 
 def pa_copy_blocks(k_cache, v_cache, cache: PaKvCache, src, dst, num_pairs, stream) -> int:
     return lib().pa_copy_blocks(k_cache, v_cache, ctypes.byref(cache), src, dst, num_pairs, stream)
+
+
+def pa_copy_blocks_layers(k_cache, v_cache, cache: PaKvCache, num_layers, src, dst, num_pairs, stream) -> int:
+    return lib().pa_copy_blocks_layers(k_cache, v_cache, ctypes.byref(cache), num_layers, src, dst, num_pairs,
+                                       stream)
 
 
 def pa_paged_attention(q, q_dtype, num_tokens, num_seqs, num_q_heads, k_cache, v_cache, cache: PaKvCache,
@@ -194,12 +201,23 @@ def write_kv(k, v, slot_mapping, k_cache, v_cache, k_scale: float = 1.0, v_scale
 
 
 def copy_blocks(k_cache, v_cache, src, dst, stream=None) -> None:
-    """pa_copy_blocks on torch tensors: block src[i] -> block dst[i] in both pools (int32 device ids)."""
+    """pa_copy_blocks on torch tensors: block src[i] -> block dst[i] in both pools (int32 device ids).
+
+    Pools of shape [num_layers, num_blocks, bs, H_kv, d] (one allocation for all layers)
+    are copied in every layer with pa_copy_blocks_layers.
+    """
     if k_cache.shape != v_cache.shape or k_cache.dtype != v_cache.dtype:
         raise ValueError("K and V pools must match")
     if src.dtype != _torch().int32 or dst.dtype != _torch().int32 or src.numel() != dst.numel():
         raise ValueError("src and dst must be int32 tensors of equal length")
     if src.numel() == 0:
+        return
+    if k_cache.dim() == 5:
+        if not k_cache.is_contiguous():
+            raise ValueError("multi-layer pools must be one contiguous allocation")
+        desc = cache_desc(k_cache[0])
+        check(pa_copy_blocks_layers(_ptr(k_cache), _ptr(v_cache), desc, k_cache.shape[0], _ptr(src), _ptr(dst),
+                                    src.numel(), _stream(stream)))
         return
     desc = cache_desc(k_cache)
     check(pa_copy_blocks(_ptr(k_cache), _ptr(v_cache), desc, _ptr(src), _ptr(dst), src.numel(), _stream(stream)))

@@ -229,9 +229,14 @@ pa_status pa_write_kv(const void* k, const void* v, int32_t in_dtype, int32_t nu
 
 pa_status pa_copy_blocks(void* k_cache, void* v_cache, const pa_kv_cache* cache, const int32_t* src,
                          const int32_t* dst, int32_t num_pairs, void* stream) {
+  return pa_copy_blocks_layers(k_cache, v_cache, cache, 1, src, dst, num_pairs, stream);
+}
+
+pa_status pa_copy_blocks_layers(void* k_cache, void* v_cache, const pa_kv_cache* cache, int32_t num_layers,
+                                const int32_t* src, const int32_t* dst, int32_t num_pairs, void* stream) {
   if (!k_cache || !v_cache || !cache || !src || !dst) return PA_ERR_NULL;
   if (const pa_status s = check_cache(cache); s != PA_OK) return s;
-  if (num_pairs < 0 || num_pairs > 65535) return PA_ERR_SHAPE;
+  if (num_pairs < 0 || num_pairs > 65535 || num_layers < 1 || num_layers > 65535) return PA_ERR_SHAPE;
   if (num_pairs == 0) return PA_OK;
   pa::CopyArgs a;
   a.k_cache = static_cast<uint8_t*>(k_cache);
@@ -241,7 +246,9 @@ pa_status pa_copy_blocks(void* k_cache, void* v_cache, const pa_kv_cache* cache,
   a.num_blocks = cache->num_blocks;
   a.block_bytes = (int64_t)cache->block_size * cache->num_kv_heads * cache->head_dim * elem_bytes(cache->dtype);
   a.chunks = a.block_bytes / 16;
+  a.layer_bytes = a.block_bytes * cache->num_blocks;
   a.num_pairs = num_pairs;
+  a.num_layers = num_layers;
   return pa::launch_copy_blocks(a, static_cast<hipStream_t>(stream)) == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 

@@ -6,6 +6,9 @@
 // whole physical block -- every row and every KV head -- of the K pool and of the
 // V pool; the bytes are copied as they are, whatever the pool format.
 //
+// Layers: a multi-layer pool is one allocation of num_layers equal pools, so a
+// copy-on-write copy moves the block in every layer; blockIdx.z is the layer.
+//
 // Workgroup (x, pair): pair = blockIdx.y, and each thread moves U 16-byte chunks
 // of K and the same chunks of V, all loads issued before the stores.  Small calls
 // (a decode step's few copies) use U = 1 to spread over more workgroups.
@@ -22,8 +25,9 @@ __global__ __launch_bounds__(kCopyThreads) void copy_blocks_kernel(const CopyArg
   const int32_t d = a.dst[blockIdx.y];
   // ids outside the pool (negative padding included) are skipped
   if (s < 0 || d < 0 || (int64_t)s >= a.num_blocks || (int64_t)d >= a.num_blocks) return;
-  const int64_t src_off = (int64_t)s * a.block_bytes;
-  const int64_t dst_off = (int64_t)d * a.block_bytes;
+  const int64_t layer_off = (int64_t)blockIdx.z * a.layer_bytes;
+  const int64_t src_off = layer_off + (int64_t)s * a.block_bytes;
+  const int64_t dst_off = layer_off + (int64_t)d * a.block_bytes;
   const int64_t c0 = (int64_t)blockIdx.x * kCopyThreads * U + threadIdx.x;
   u32x4 kx[U], vx[U];
 #pragma unroll
@@ -47,14 +51,14 @@ __global__ __launch_bounds__(kCopyThreads) void copy_blocks_kernel(const CopyArg
 template <int U>
 static void launch_u(const CopyArgs& a, hipStream_t stream) {
   const int64_t per_wg = (int64_t)kCopyThreads * U;
-  const dim3 grid((unsigned)((a.chunks + per_wg - 1) / per_wg), (unsigned)a.num_pairs);
+  const dim3 grid((unsigned)((a.chunks + per_wg - 1) / per_wg), (unsigned)a.num_pairs, (unsigned)a.num_layers);
   hipLaunchKernelGGL(copy_blocks_kernel<U>, grid, dim3(kCopyThreads), 0, stream, a);
 }
 
 hipError_t launch_copy_blocks(const CopyArgs& a, hipStream_t stream) {
   if (a.num_pairs == 0) return hipSuccess;
   // enough chunks to fill the chip several times over: unroll; otherwise one chunk per thread
-  if ((int64_t)a.num_pairs * a.chunks >= (int64_t)256 * kCopyThreads * 4 * 8) launch_u<4>(a, stream);
+  if ((int64_t)a.num_pairs * a.num_layers * a.chunks >= (int64_t)256 * kCopyThreads * 4 * 8) launch_u<4>(a, stream);
   else launch_u<1>(a, stream);
   return hipGetLastError();
 }

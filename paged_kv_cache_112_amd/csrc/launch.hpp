@@ -77,7 +77,9 @@ struct CopyArgs {
   int64_t num_blocks;
   int64_t block_bytes;       // bs * H_kv * D * elem, a multiple of 16
   int64_t chunks;            // block_bytes / 16
+  int64_t layer_bytes;       // multi-layer pools: distance between layers' pools (0 for one layer)
   int32_t num_pairs;
+  int32_t num_layers;
 };
 
 struct AttnArgs {

@@ -168,3 +168,8 @@ def test_copy_blocks_checks(kw, status):
     if a["num_pairs"] != 0 and status == pa.PA_OK:
         pytest.skip("a valid call would launch")
     assert pa.pa_copy_blocks(**a) == status
+
+
+@pytest.mark.parametrize("layers,status", [(0, pa.PA_ERR_SHAPE), (65536, pa.PA_ERR_SHAPE), (-2, pa.PA_ERR_SHAPE)])
+def test_copy_blocks_layers_checks(layers, status):
+    assert pa.pa_copy_blocks_layers(FAKE, FAKE, _cache(dtype=pa.PA_BF16), layers, FAKE, FAKE, 3, None) == status

@@ -5,7 +5,7 @@ import pytest
 import oracle
 from pools import POISON, STORAGE, build_host_inputs, from_dev, out_to_f64, to_dev
 from test_cow import cow_scenario
-from workloads import make_config
+from workloads import f32_to_bf16_bits, make_config
 
 pytestmark = pytest.mark.gpu
 
@@ -86,3 +86,46 @@ def test_copy_blocks_full_size_fp8_pool():
     oracle.copy_blocks(kc, vc, src, dst)
     assert np.array_equal(from_dev(dk), kc)
     assert np.array_equal(from_dev(dv), vc)
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "e4m3", "i8"])
+def test_multi_layer_pool_in_one_allocation(fmt):
+    """Pools [L, nb, bs, H_kv, d] in one allocation: per-layer writes and decodes through layer views,
+    and copy-on-write copies of every layer in one launch."""
+    import torch
+    import paged_kv_cache_112_amd as pa
+    from pools import POISON, STORAGE
+    L, nb, bs, hkv, d, hq = 3, 24, 16, 2, 128, 8
+    rng = np.random.default_rng(21)
+    kc = np.full((L, nb, bs, hkv, d), POISON[fmt], dtype=STORAGE[fmt])
+    vc = np.full_like(kc, POISON[fmt])
+    ctx = np.array([40, 17, 64], dtype=np.int32)
+    bt = np.array([[3, 9, 1, 0], [5, 2, 0, 0], [7, 11, 13, 4]], dtype=np.int32)
+    scale_k = scale_v = 1.0 if fmt == "bf16" else (0.02 if fmt == "e4m3" else 0.03)
+    dk, dv = to_dev(kc), to_dev(vc)
+    for l in range(L):                              # each layer's own values, written through its view
+        for b, c in enumerate(ctx):
+            pos = np.arange(c)
+            kk = f32_to_bf16_bits(rng.standard_normal((c, hkv, d)).astype(np.float32))
+            vv = f32_to_bf16_bits(rng.standard_normal((c, hkv, d)).astype(np.float32))
+            slots = (bt[b, pos // bs] * bs + pos % bs).astype(np.int32)
+            oracle.write_kv(kc[l], vc[l], kk, vv, slots, fmt, "bf16", scale_k, scale_v)
+            pa.write_kv(to_dev(kk), to_dev(vv), to_dev(slots), dk[l], dv[l], scale_k, scale_v)
+    src = np.array([9, 13], dtype=np.int32)
+    dst = np.array([20, 21], dtype=np.int32)
+    pa.copy_blocks(dk, dv, to_dev(src), to_dev(dst))
+    for l in range(L):
+        oracle.copy_blocks(kc[l], vc[l], src, dst)
+    torch.cuda.synchronize()
+    assert np.array_equal(from_dev(dk).view(np.uint8), kc.view(np.uint8))
+    assert np.array_equal(from_dev(dv).view(np.uint8), vc.view(np.uint8))
+    # sequences 0 and 2 now read the copies: same values, other blocks
+    bt2 = bt.copy()
+    bt2[0, 1], bt2[2, 2] = 20, 21
+    q = f32_to_bf16_bits(rng.standard_normal((3, hq, d)).astype(np.float32))
+    for l in range(L):
+        out = pa.decode(to_dev(q), dk[l], dv[l], to_dev(bt2), to_dev(ctx), 0.088, max_context_len=64,
+                        k_scale=scale_k, v_scale=scale_v)
+        torch.cuda.synchronize()
+        ref = oracle.decode(q, kc[l], vc[l], bt, ctx, 0.088, fmt, "bf16", scale_k, scale_v)
+        assert np.abs(out_to_f64(out) - ref).max() <= 2e-2
