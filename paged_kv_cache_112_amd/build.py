@@ -32,6 +32,14 @@ COMMON_FLAGS = [
     "-I" + os.path.join(ROOT, "include"),
 ]
 
+# Per-source additions.  The multi-query attention kernel keeps its matrix-core
+# accumulators in ordinary VGPRs: its rare rescale multiplies them on the vector unit,
+# and with accumulation registers the compiler copies every accumulator between the two
+# register files at each loop iteration.
+SOURCE_FLAGS = {
+    "attention_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
+
 
 def hipcc() -> str:
     for cand in (os.environ.get("HIPCC"), shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
@@ -59,7 +67,7 @@ def build(verbose: bool = False, extra_flags: list[str] | None = None, out_path:
     for src in SOURCES:
         obj = os.path.join(obj_dir, os.path.splitext(src)[0] + ".o")
         objs.append(obj)
-        jobs.append(([cc, *flags, "-c", os.path.join(CSRC, src), "-o", obj], src))
+        jobs.append(([cc, *flags, *SOURCE_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj], src))
     workers = max(1, min(len(jobs), int(os.environ.get("MAX_JOBS", "8"))))
     with ThreadPoolExecutor(workers) as ex:
         for log in ex.map(_compile, jobs):

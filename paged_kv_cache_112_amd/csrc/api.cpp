@@ -293,8 +293,8 @@ pa_status pa_paged_attention(const void* q, int32_t q_dtype, int32_t num_tokens,
   const float ks = is_scaled(cache->dtype) ? cache->k_scale : 1.0f;
   a.qk_scale = scale * kLog2e * ks;
   a.v_scale = is_scaled(cache->dtype) ? cache->v_scale : 1.0f;
-  const int64_t tiles = ((int64_t)max_query_len + (16 >> a.log2_group) - 1) / (16 >> a.log2_group);
-  if ((tiles + 3) / 4 * a.num_kv_heads > INT32_MAX) return PA_ERR_SHAPE;
+  const int64_t per_wg = pa::attention_tokens_per_workgroup(a.log2_group);
+  if (((int64_t)max_query_len + per_wg - 1) / per_wg * a.num_kv_heads > INT32_MAX) return PA_ERR_SHAPE;
   return pa::launch_attention_mfma(a, static_cast<hipStream_t>(stream)) == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 

@@ -1,5 +1,5 @@
 // Multi-query paged attention (chunked prefill, or several new tokens per sequence),
-// matrix-core path: bf16 q with a bf16 or e4m3 pool.
+// matrix-core path: bf16 q with a bf16, e4m3 or int8 pool.
 //
 // What is computed: request i's new tokens are q[qsl[i] .. qsl[i+1]), the last
 // n_i = qsl[i+1] - qsl[i] positions of its context of S_i = seq_lens[i] tokens; new
@@ -10,71 +10,107 @@
 // block_tables, seq_lens and query_start_loc, the lower-triangular mask offset by
 // S - n, and the statement that the math equals contiguous attention).
 //
-// How, on gfx950: one wave per (request, KV head, query tile).  A query tile is
-// T = 16 / G new tokens with all G query heads of the KV head, so the 16 columns of
-// the MFMA B operand are (token, head) pairs and the product is dense.  The four
-// waves of a workgroup take four consecutive query tiles of the same KV head, so a
-// K/V tile fetched by one of them is found in the CU's cache by the others.
-//   * q.K^T: v_mfma_f32_16x16x32_bf16 with A = a 16-key tile (row = key), B = q^T
-//     (column n = token n / G, head n % G), as in the decode kernel.
-//   * Softmax runs online over the key tiles in base 2, per column: a running max m,
-//     and whenever m grows the running sum and output are scaled by 2^(m_old - m_new).
-//   * P.V is the transposed product O^T = V^T P^T (v_mfma_f32_16x16x16_bf16), whose
-//     output keeps each column's values in that column's own lanes, so the rescale is
-//     a lane-local multiply.
-// Keys past the causal limit of a column get probability 0; the key loop stops at
-// the last tile any column of the tile can see.  Rows past the context are clamped
-// to the last valid row for addressing.
+// How, on gfx950: one wave per (request, KV head, run of NQ query groups).  A query
+// group is T = 16 / G new tokens with all G query heads of the KV head: the 16
+// columns of one MFMA operand, (token, head) pairs, so the product is dense.  Each
+// K/V tile a wave loads (and, for one-byte pools, widens) serves all NQ groups.  The
+// four waves of a workgroup take consecutive runs of the same KV head, so a tile one
+// of them fetches is found in the CU's cache by the others.
+//   * Keys advance 32 per step, as two 16-key tiles a and b.
+//   * q.K^T: v_mfma_f32_16x16x32_bf16 with A = a 16-key tile (row = key), B = q^T.
+//   * P.V is the transposed product O^T = V^T P^T, on v_mfma_f32_16x16x32_bf16 over
+//     the step's 32 keys: k-slot 8*q4 + j is key 4*q4 + j of tile a (j < 4) or key
+//     4*q4 + j - 4 of tile b, which is where q.K^T left each lane's probabilities, so
+//     they become the B operand without moving between lanes.  The output keeps each
+//     column's values in that column's own lanes, so rescaling is lane-local.
+//   * Softmax runs online in base 2 with a lazy reference: a column's running max m
+//     is raised only when a step's max exceeds it by more than kRescaleLog2, so the
+//     probabilities exp2(x - m) stay below 2^kRescaleLog2 and the output and sum are
+//     rescaled only on those (rare, wave-uniform) steps.  Numerator and denominator
+//     use the same reference, so the quotient is the softmax.
+//   * Steps wholly below the causal limit of every column of the wave skip the mask.
+// Rows past the context are clamped to the last valid row for addressing.
 #include "launch.hpp"
 #include "mfma_tiles.hpp"
 
 namespace pa {
 
-constexpr int kAttnWaves = 4;   // query tiles (waves) per workgroup
+constexpr int kAttnWaves = 4;          // query runs (waves) per workgroup
+constexpr float kRescaleLog2 = 8.0f;   // lazy-rescale threshold, in log2 units
 
 __device__ __forceinline__ int32_t attn_load_uniform(const int32_t* p) {
   return *(const __attribute__((address_space(4))) int32_t*)p;
 }
 
-template <int KF, int D, bool BIGBS>
+// Maximum over the four lanes n, n+16, n+32, n+48 (gfx950 permlane swaps).
+__device__ __forceinline__ float col_max(float x) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+// Two floats to a bf16 pair, round to nearest even (one packed convert).
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t cvt_bf16x2(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
+}
+
+// Element e (0 .. 2*NW-1) of a row of NW packed bf16 pairs, for rows lo and hi, packed
+// into one pair.
+template <int NW>
+__device__ __forceinline__ uint32_t pair_of(const uint32_t (&lo)[NW], const uint32_t (&hi)[NW], int e) {
+  return (e & 1) ? pack_hi_halves(lo[e >> 1], hi[e >> 1]) : pack_lo_halves(lo[e >> 1], hi[e >> 1]);
+}
+
+template <int KF, int D, bool BIGBS, int NQ>
 __global__ __launch_bounds__(256) void attention_mfma_kernel(const AttnArgs a) {
   constexpr int ESZ = byte_fmt(KF) ? 1 : 2;
   constexpr int VEC = D / 16;
   constexpr int NKK = D / 32;
+  // q^T operands of every wave, in the order the lanes read them (conflict-free)
+  __shared__ u32x4 q_lds[kAttnWaves][NQ][NKK][kWave];
+
   const int kvh = blockIdx.x % a.num_kv_heads;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int qt = (blockIdx.x / a.num_kv_heads) * kAttnWaves + wave;
   const int i = blockIdx.y;
-  const int q0 = a.query_start_loc[i];
-  const int nq = a.query_start_loc[i + 1] - q0;
-  const int S = a.seq_lens[i];
-  const int T = 16 >> a.log2_group;                 // query tokens per tile
-  const int t0 = qt * T;
-  // whole workgroup (uniform): past this request's queries, or inconsistent lengths
-  if (t0 >= nq || nq > S || q0 < 0 || q0 + nq > a.num_tokens) return;   // per wave: no barrier follows
+  const int q0 = attn_load_uniform(a.query_start_loc + i);
+  const int nq = attn_load_uniform(a.query_start_loc + i + 1) - q0;
+  const int S = attn_load_uniform(a.seq_lens + i);
+  const int T = 16 >> a.log2_group;                 // query tokens per group
+  const int t0 = ((blockIdx.x / a.num_kv_heads) * kAttnWaves + wave) * (NQ * T);
+  // past this request's queries, or inconsistent lengths (uniform per wave; no barrier follows)
+  if (t0 >= nq || nq > S || q0 < 0 || q0 + nq > a.num_tokens) return;
 
   const int lane = threadIdx.x & 63;
   const int G = 1 << a.log2_group;
   const int n = lane & 15;
   const int q4 = lane >> 4;
-  const int tq = t0 + (n >> a.log2_group);          // this column's query token (request-local)
   const int g = n & (G - 1);
-  const bool qvalid = tq < nq;
-  const int qpos = S - nq + tq;                     // its position in the context
-  const int tlast = min(t0 + T, nq) - 1;
-  const int kmax = S - nq + tlast;                  // last key any column of the tile sees
-  const int nkt = (kmax >> 4) + 1;
+  const int tn = n >> a.log2_group;                 // token offset within a group
+  const int base = S - nq;                          // context position of new token 0
+  const int kend = base + min(t0 + NQ * T, nq);     // keys [0, kend) cover every column
+  const int nst = (kend + 31) >> 5;
+  const int nfull = (base + t0 + 1) >> 5;           // steps every column sees whole
+  // The scale enters as sc > 0: a negative scale is a sign flip of q (exact) and a zero
+  // scale is q = 0 with sc = 1 (every score 0), so maxima of raw scores order the
+  // scaled ones and a masked score of -inf gives exactly 0.
+  const float sc = a.qk_scale == 0.f ? 1.f : fabsf(a.qk_scale);
+  const uint32_t qflip = a.qk_scale < 0.f ? 0x80008000u : 0u;
+  const bool qzero = a.qk_scale == 0.f;
 
-  // q^T as the B operand: lane (n, q4) holds 8 d's of (token tq, head g)
-  bf16x8 qB[NKK];
-  {
+  int qpos[NQ];
+#pragma unroll
+  for (int c = 0; c < NQ; ++c) {
+    const int tq = t0 + c * T + tn;
+    qpos[c] = base + tq;
     const uint16_t* qrow = static_cast<const uint16_t*>(a.q) +
                            ((int64_t)(q0 + min(tq, nq - 1)) * a.num_q_heads + kvh * G + g) * D;
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
       u32x4 w = {0u, 0u, 0u, 0u};
-      if (qvalid) w = ld16(qrow + q_col<KF, D>(kk, q4));
-      qB[kk] = __builtin_bit_cast(bf16x8, w);
+      if (tq < nq && !qzero) w = ld16(qrow + q_col<KF, D>(kk, q4)) ^ qflip;
+      q_lds[wave][c][kk][lane] = w;
     }
   }
 
@@ -83,102 +119,253 @@ __global__ __launch_bounds__(256) void attention_mfma_kernel(const AttnArgs a) {
   const uint8_t* kbase = a.k_cache + head_off;
   const uint8_t* vbase = a.v_cache + head_off;
   const int bs_mask = a.block_size - 1;
-  // byte offset of key t (clamped to the context) within the pool
-  auto row_off = [&](int t, int tile) -> int64_t {
-    const int tc = min(t, S - 1);
-    int32_t blk;
-    if constexpr (BIGBS) blk = attn_load_uniform(bt_row + (min(16 * tile, S - 1) >> a.log2_bs));
-    else blk = bt_row[tc >> a.log2_bs];
-    return (int64_t)blk * a.block_bytes + (int64_t)(tc & bs_mask) * a.row_bytes;
-  };
-  auto load_k = [&](int kt) {
-    KTile<KF, D> t;
-    const uint8_t* p = kbase + row_off(16 * kt + n, kt) + 16 * q4;
+  const uint32_t row_bytes = (uint32_t)a.row_bytes;
+  // per-lane byte offsets within a 16-key tile: K row n; V rows 4*q4 + j
+  const uint32_t k_lane = (uint32_t)n * row_bytes + 16 * q4;
+  uint32_t v_lane[4];
 #pragma unroll
-    for (int j = 0; j < KTile<KF, D>::N; ++j) t.w[j] = ld16(p + 64 * j);
-    return t;
+  for (int j = 0; j < 4; ++j) v_lane[j] = (uint32_t)(4 * q4 + j) * row_bytes + n * VEC * ESZ;
+
+  // Address of tile `tile`'s key 16*tile + r plus `lane_bytes`, key clamped to the context.
+  auto row_ptr = [&](const uint8_t* base, int r, int tile, uint32_t lane_bytes) -> const uint8_t* {
+    const int tc = min(16 * tile + r, S - 1);
+    if constexpr (BIGBS) {
+      const int32_t blk = attn_load_uniform(bt_row + (min(16 * tile, S - 1) >> a.log2_bs));
+      return base + (int64_t)blk * a.block_bytes + (size_t)((uint32_t)(tc & bs_mask) * row_bytes + lane_bytes);
+    } else {
+      const int32_t blk = bt_row[tc >> a.log2_bs];
+      return base + (int64_t)blk * a.block_bytes + (size_t)((uint32_t)(tc & bs_mask) * row_bytes + lane_bytes);
+    }
   };
-  auto load_v = [&](int kt) {
-    VTile<KF, D> t;
+  // K or V tiles of step st (keys 32*st .. 32*st + 31).  With blocks of 16 tokens or
+  // more, a step inside the context has each of its two tiles in one block at a uniform
+  // offset, the same for K and V: scalar base plus the per-lane constant offsets.
+  struct StepAddr {
+    int64_t off[2];
+    bool fast;
+  };
+  auto step_addr = [&](int st) {
+    StepAddr t;
+    t.fast = BIGBS && 32 * st + 32 <= S;
+    if (t.fast) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint8_t* p = vbase + row_off(16 * kt + 4 * q4 + j, kt) + n * VEC * ESZ;
-      t.w[j] = *reinterpret_cast<const typename VTile<KF, D>::W*>(p);
+      for (int h = 0; h < 2; ++h) {
+        const int key = 32 * st + 16 * h;
+        const int32_t blk = attn_load_uniform(bt_row + (key >> a.log2_bs));
+        t.off[h] = (int64_t)blk * a.block_bytes + (int64_t)((uint32_t)(key & bs_mask) * row_bytes);
+      }
     }
     return t;
+  };
+  auto load_k = [&](KTile<KF, D> (&k)[2], int st, const StepAddr& t) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int tile = 2 * st + h;
+      const uint8_t* pk = t.fast ? kbase + t.off[h] + k_lane : row_ptr(kbase, n, tile, 16 * q4);
+#pragma unroll
+      for (int j = 0; j < KTile<KF, D>::N; ++j) k[h].w[j] = ld16(pk + 64 * j);
+    }
+  };
+  auto load_v = [&](VTile<KF, D> (&v)[2], int st, const StepAddr& t) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int tile = 2 * st + h;
+      if (t.fast) {
+        const uint8_t* vb = vbase + t.off[h];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) v[h].w[j] = *reinterpret_cast<const typename VTile<KF, D>::W*>(vb + v_lane[j]);
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint8_t* pv = row_ptr(vbase, 4 * q4 + j, tile, n * VEC * ESZ);
+          v[h].w[j] = *reinterpret_cast<const typename VTile<KF, D>::W*>(pv);
+        }
+      }
+    }
   };
 
-  f32x4 O[VEC];
+  f32x4 O[NQ][VEC];
+  f32x4 L[NQ];        // column sums of the probabilities (every register the same)
+  float m[NQ];        // reference max per column, scaled log2 domain
+  float thr[NQ];      // raw score above which the reference must be raised
 #pragma unroll
-  for (int e = 0; e < VEC; ++e) O[e] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m = -INFINITY, lsum = 0.f;
-  KTile<KF, D> kc = load_k(0);
-  VTile<KF, D> vc = load_v(0);
-  for (int kt = 0; kt < nkt; ++kt) {
-    KTile<KF, D> kn;
-    VTile<KF, D> vn;
-    if (kt + 1 < nkt) {                             // next tile in flight while this one computes
-      kn = load_k(kt + 1);
-      vn = load_v(kt + 1);
-    }
-    const f32x4 s = qk_tile<KF, D>(kc, qB);
-    float x[4];
+  for (int c = 0; c < NQ; ++c) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int key = 16 * kt + 4 * q4 + r;
-      x[r] = (qvalid && key <= qpos) ? s[r] * a.qk_scale : -INFINITY;
-    }
-    float mt = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-    mt = fmaxf(mt, __shfl_xor(mt, 16));
-    mt = fmaxf(mt, __shfl_xor(mt, 32));
-    const float m_new = fmaxf(m, mt);
-    const float mref = m_new == -INFINITY ? 0.f : m_new;     // a column with no visible key yet
-    const float alpha = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - mref);
-    m = m_new;
-    float p[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      // probabilities enter P.V as bf16; the denominator sums the same rounded values
-      p[r] = (float)(__bf16)__builtin_amdgcn_exp2f(x[r] - mref);
-    }
-    lsum = lsum * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
-#pragma unroll
-    for (int e = 0; e < VEC; ++e) O[e] *= alpha;
-    pvt_tile<KF, D>(vc, pack_bf16(p[0], p[1]), pack_bf16(p[2], p[3]), O);
-    if (kt + 1 < nkt) {
-      kc = kn;
-      vc = vn;
-    }
+    for (int e = 0; e < VEC; ++e) O[c][e] = f32x4{0.f, 0.f, 0.f, 0.f};
+    L[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+    m[c] = -INFINITY;
+    thr[c] = -INFINITY;
   }
-  lsum += __shfl_xor(lsum, 16);
-  lsum += __shfl_xor(lsum, 32);
+  const bf16x8 ones = __builtin_bit_cast(bf16x8, u32x4{0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u});
+  const float inv_sc = 1.f / sc;
+  // q.K^T and the softmax of step st for every group: the probabilities as B operands
+  auto scores = [&](auto masked_tag, const KTile<KF, D> (&kt)[2], int st, bf16x8 (&pB)[NQ]) {
+    constexpr bool MASKED = decltype(masked_tag)::value;
+    // K operands, widened once for every group
+    bf16x8 kop[2][NKK];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      if constexpr (!byte_fmt(KF)) {
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk) kop[h][kk] = __builtin_bit_cast(bf16x8, kt[h].w[kk]);
+      } else {
+#pragma unroll
+        for (int j = 0; j < KTile<KF, D>::N; ++j) {
+          kop[h][2 * j] = bytes8_to_bf16x8<KF>(kt[h].w[j][0], kt[h].w[j][1]);
+          kop[h][2 * j + 1] = bytes8_to_bf16x8<KF>(kt[h].w[j][2], kt[h].w[j][3]);
+        }
+      }
+    }
+    // The q operands are read from LDS at each step (an empty asm makes their address
+    // opaque, so they are not hoisted out of the loop into registers).
+    const __attribute__((address_space(3))) u32x4* qw =
+        (const __attribute__((address_space(3))) u32x4*)&q_lds[wave][0][0][lane];
+    asm volatile("" : "+v"(qw));
+    // q.K^T of group c: s[h] register r = score of key 32*st + 16*h + 4*q4 + r, column n
+    auto qk = [&](int c, f32x4 (&s)[2]) {
+      s[0] = f32x4{0.f, 0.f, 0.f, 0.f};
+      s[1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk) {
+        const bf16x8 qb = __builtin_bit_cast(bf16x8, qw[(c * NKK + kk) * kWave]);
+        s[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[0][kk], qb, s[0], 0, 0, 0);
+        s[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[1][kk], qb, s[1], 0, 0, 0);
+      }
+    };
+    // group by group: the next group's q.K^T is issued before this group's softmax, so
+    // the matrix core works while the vector unit does the softmax
+    f32x4 sn[2];
+    qk(0, sn);
+#pragma unroll
+    for (int c = 0; c < NQ; ++c) {
+      f32x4 s[2] = {sn[0], sn[1]};
+      if (c + 1 < NQ) qk(c + 1, sn);
+      if constexpr (MASKED) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (32 * st + 16 * h + 4 * q4 + r > qpos[c]) s[h][r] = -INFINITY;
+      }
+      bool grow = false;
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) grow |= s[h][r] > thr[c];
+      if (__builtin_amdgcn_ballot_w64(grow) != 0) {   // uniform: raise this group's references
+        const float v = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
+                              fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
+        const float mn = fmaxf(m[c], col_max(v) * sc);
+        const float mref = mn == -INFINITY ? 0.f : mn;   // a column with no visible key yet
+        const float alpha = __builtin_amdgcn_exp2f(m[c] - mref);
+        m[c] = mref;
+        thr[c] = (mref + kRescaleLog2) * inv_sc;
+        L[c] *= alpha;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) O[c][e] *= alpha;
+      }
+      float p[2][4];
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) p[h][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[h][r], sc, -m[c]));
+      pB[c] = __builtin_bit_cast(bf16x8, u32x4{cvt_bf16x2(p[0][0], p[0][1]), cvt_bf16x2(p[0][2], p[0][3]),
+                                               cvt_bf16x2(p[1][0], p[1][1]), cvt_bf16x2(p[1][2], p[1][3])});
+      L[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pB[c], L[c], 0, 0, 0);
+    }
+  };
+  // O += P.V of one step for every group
+  auto accumulate = [&](const VTile<KF, D> (&vt)[2], const bf16x8 (&pB)[NQ]) {
+    // V rows as bf16 pairs: rw[h][j][w] = columns 2w, 2w+1 of row 4*q4 + j of tile h
+    constexpr int NW = VEC / 2;
+    uint32_t rw[2][4][NW];
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if constexpr (!byte_fmt(KF)) {
+#pragma unroll
+          for (int w = 0; w < NW; ++w) rw[h][j][w] = vt[h].w[j][w];
+        } else if constexpr (VEC == 8) {
+          rw[h][j][0] = bytes2_to_bf16x2<KF>(vt[h].w[j][0], false);
+          rw[h][j][1] = bytes2_to_bf16x2<KF>(vt[h].w[j][0], true);
+          rw[h][j][2] = bytes2_to_bf16x2<KF>(vt[h].w[j][1], false);
+          rw[h][j][3] = bytes2_to_bf16x2<KF>(vt[h].w[j][1], true);
+        } else {
+          rw[h][j][0] = bytes2_to_bf16x2<KF>(vt[h].w[j], false);
+          rw[h][j][1] = bytes2_to_bf16x2<KF>(vt[h].w[j], true);
+        }
+      }
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) {
+      // A = V^T block e: row m = head-dimension index VEC*m + e, k-slots as pB
+      const bf16x8 A = __builtin_bit_cast(bf16x8, u32x4{pair_of<NW>(rw[0][0], rw[0][1], e), pair_of<NW>(rw[0][2], rw[0][3], e),
+                                                        pair_of<NW>(rw[1][0], rw[1][1], e), pair_of<NW>(rw[1][2], rw[1][3], e)});
+#pragma unroll
+      for (int c = 0; c < NQ; ++c) O[c][e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, pB[c], O[c][e], 0, 0, 0);
+    }
+  };
 
-  // lane (n, q4) register r of O[e] holds column n's output at d = VEC*(4*q4 + r) + e
-  if (qvalid) {
-    const float inv = a.v_scale / lsum;
-    uint16_t* o = static_cast<uint16_t*>(a.out) + ((int64_t)(q0 + tq) * a.num_q_heads + kvh * G + g) * D;
+  // One K and one V buffer: the next step's K is requested as soon as q.K^T has read
+  // the current one, and its V as soon as P.V has; the step after the last loads
+  // clamped rows.  Steps that every column sees whole run without the mask.
+  KTile<KF, D> k[2];
+  VTile<KF, D> v[2];
+  auto step = [&](auto masked_tag, int st) {
+    const StepAddr next = step_addr(st + 1);
+    bf16x8 pB[NQ];
+    scores(masked_tag, k, st, pB);
+    load_k(k, st + 1, next);
+    accumulate(v, pB);
+    load_v(v, st + 1, next);
+  };
+  {
+    const StepAddr first = step_addr(0);
+    load_k(k, 0, first);
+    load_v(v, 0, first);
+  }
+  int st = 0;
+  for (; st < nfull; ++st) step(std::false_type{}, st);
+  for (; st < nst; ++st) step(std::true_type{}, st);
+
+  // lane (n, q4) register r of O[c][e] holds group c column n at d = VEC*(4*q4 + r) + e
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      uint32_t w[VEC / 2];
+  for (int c = 0; c < NQ; ++c) {
+    const int tq = t0 + c * T + tn;
+    if (tq < nq) {
+      const float inv = a.v_scale / L[c][0];
+      uint16_t* o = static_cast<uint16_t*>(a.out) + ((int64_t)(q0 + tq) * a.num_q_heads + kvh * G + g) * D;
 #pragma unroll
-      for (int c = 0; c < VEC / 2; ++c) w[c] = pack_bf16(O[2 * c][r] * inv, O[2 * c + 1][r] * inv);
-      uint16_t* dst = o + VEC * (4 * q4 + r);
-      if constexpr (VEC == 8) st16(dst, u32x4{w[0], w[1], w[2], w[3]});
-      else st8(dst, u32x2{w[0], w[1]});
+      for (int r = 0; r < 4; ++r) {
+        uint32_t w[VEC / 2];
+#pragma unroll
+        for (int x = 0; x < VEC / 2; ++x) w[x] = cvt_bf16x2(O[c][2 * x][r] * inv, O[c][2 * x + 1][r] * inv);
+        uint16_t* dst = o + VEC * (4 * q4 + r);
+        if constexpr (VEC == 8) st16(dst, u32x4{w[0], w[1], w[2], w[3]});
+        else st8(dst, u32x2{w[0], w[1]});
+      }
     }
   }
 }
+
+// query groups per wave
+#ifndef PA_ATTN_NQ
+#define PA_ATTN_NQ 4
+#endif
+constexpr int kAttnNq = PA_ATTN_NQ;
 
 template <int KF, int D>
 static void launch_d(const AttnArgs& a, dim3 grid, dim3 block, hipStream_t s) {
-  if (a.block_size >= 16) hipLaunchKernelGGL((attention_mfma_kernel<KF, D, true>), grid, block, 0, s, a);
-  else hipLaunchKernelGGL((attention_mfma_kernel<KF, D, false>), grid, block, 0, s, a);
+  if (a.block_size >= 16) hipLaunchKernelGGL((attention_mfma_kernel<KF, D, true, kAttnNq>), grid, block, 0, s, a);
+  else hipLaunchKernelGGL((attention_mfma_kernel<KF, D, false, kAttnNq>), grid, block, 0, s, a);
 }
 
+int attention_tokens_per_workgroup(int log2_group) { return kAttnWaves * kAttnNq * (16 >> log2_group); }
+
 hipError_t launch_attention_mfma(const AttnArgs& a, hipStream_t s) {
-  const int T = 16 >> a.log2_group;
-  const int tiles = (a.max_query_len + T - 1) / T;
-  const dim3 grid((unsigned)(((tiles + kAttnWaves - 1) / kAttnWaves) * a.num_kv_heads), (unsigned)a.num_seqs);
+  const int per_wg = attention_tokens_per_workgroup(a.log2_group);
+  const int wgs = (a.max_query_len + per_wg - 1) / per_wg;
+  const dim3 grid((unsigned)(wgs * a.num_kv_heads), (unsigned)a.num_seqs);
   const dim3 block((unsigned)(kWave * kAttnWaves));
   const bool d128 = a.head_dim == 128;
   switch (a.kv_fmt) {

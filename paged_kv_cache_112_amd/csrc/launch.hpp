@@ -108,6 +108,8 @@ struct SlotArgs {
 hipError_t launch_write_kv(const WriteArgs& a, hipStream_t stream);
 hipError_t launch_slot_mapping(const SlotArgs& a, hipStream_t stream);
 hipError_t launch_attention_mfma(const AttnArgs& a, hipStream_t stream);
+// new tokens of one request handled by one workgroup of the multi-query kernel
+int attention_tokens_per_workgroup(int log2_group);
 hipError_t launch_copy_blocks(const CopyArgs& a, hipStream_t stream);
 hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_decode_persist(const DecodeArgs& a, hipStream_t stream);

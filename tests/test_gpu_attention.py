@@ -16,7 +16,7 @@ pytestmark = pytest.mark.gpu
 class MQ:
     """Host pools (written by the oracle), tables and queries for one multi-query call."""
 
-    def __init__(self, seq_lens, qlens, hq, hkv, d, bs, kv="bf16", seed=0, tables=None, nb=None):
+    def __init__(self, seq_lens, qlens, hq, hkv, d, bs, kv="bf16", seed=0, tables=None, nb=None, kgrow=0.0):
         rng = np.random.default_rng(seed)
         self.seq_lens = np.asarray(seq_lens, dtype=np.int32)
         self.qsl = np.concatenate([[0], np.cumsum(qlens)]).astype(np.int32)
@@ -35,6 +35,9 @@ class MQ:
         self.vc = np.full_like(self.kc, POISON[kv])
         self.ks = self.vs = 1.0
         kvals = [rng.standard_normal((int(s), hkv, d)).astype(np.float32) for s in seq_lens]
+        if kgrow:                                     # key norms growing with the position
+            kvals = [(x * (1.0 + kgrow * np.arange(len(x), dtype=np.float32))[:, None, None]).astype(np.float32)
+                     for x in kvals]
         vvals = [rng.standard_normal((int(s), hkv, d)).astype(np.float32) for s in seq_lens]
         if kv in ("e4m3", "i8"):
             qmax = 448.0 if kv == "e4m3" else 127.0
@@ -87,6 +90,23 @@ def test_peaky_scores(kv):
     """A large scale makes each row nearly one-hot: a wrong key or mask shows as an O(1) error."""
     m = MQ([70, 33, 129], [70, 9, 20], 32, 8, 128, 16, kv, seed=9)
     scale = float(np.float32(8 / np.sqrt(128)))
+    assert np.abs(out_to_f64(m.run(scale)) - m.oracle(scale)).max() <= 2e-2
+
+
+@pytest.mark.parametrize("scale", [-0.0883883, 0.0, -0.7])
+def test_negative_and_zero_scale(scale):
+    """The kernel applies a negative scale as a sign flip of q; a zero scale gives the mean of visible rows."""
+    m = MQ([50, 300, 33], [50, 70, 9], 32, 8, 128, 16, seed=13)
+    scale = float(np.float32(scale))
+    assert np.abs(out_to_f64(m.run(scale)) - m.oracle(scale)).max() <= 2e-2
+
+
+@pytest.mark.parametrize("kv", ["bf16", "i8"])
+def test_scores_growing_along_the_context(kv):
+    """Key norms growing with the position push the running maximum up step after step, so
+    the output and sum are re-referenced many times within one query's pass."""
+    m = MQ([600, 200, 97], [64, 200, 30], 32, 8, 128, 16, kv, seed=17, kgrow=0.05)
+    scale = float(np.float32(1 / np.sqrt(128)))
     assert np.abs(out_to_f64(m.run(scale)) - m.oracle(scale)).max() <= 2e-2
 
 
