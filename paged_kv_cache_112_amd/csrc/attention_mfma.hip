@@ -50,12 +50,6 @@ __device__ __forceinline__ float col_max(float x) {
   return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
-// Two floats to a bf16 pair, round to nearest even (one packed convert).
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-__device__ __forceinline__ uint32_t cvt_bf16x2(float lo, float hi) {
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
-}
-
 // Element e (0 .. 2*NW-1) of a row of NW packed bf16 pairs, for rows lo and hi, packed
 // into one pair.
 template <int NW>
@@ -287,13 +281,13 @@ __global__ __launch_bounds__(256) void attention_mfma_kernel(const AttnArgs a) {
 #pragma unroll
           for (int w = 0; w < NW; ++w) rw[h][j][w] = vt[h].w[j][w];
         } else if constexpr (VEC == 8) {
-          rw[h][j][0] = bytes2_to_bf16x2<KF>(vt[h].w[j][0], false);
-          rw[h][j][1] = bytes2_to_bf16x2<KF>(vt[h].w[j][0], true);
-          rw[h][j][2] = bytes2_to_bf16x2<KF>(vt[h].w[j][1], false);
-          rw[h][j][3] = bytes2_to_bf16x2<KF>(vt[h].w[j][1], true);
+          rw[h][j][0] = bytes2_to_bf16x2<KF, false>(vt[h].w[j][0]);
+          rw[h][j][1] = bytes2_to_bf16x2<KF, true>(vt[h].w[j][0]);
+          rw[h][j][2] = bytes2_to_bf16x2<KF, false>(vt[h].w[j][1]);
+          rw[h][j][3] = bytes2_to_bf16x2<KF, true>(vt[h].w[j][1]);
         } else {
-          rw[h][j][0] = bytes2_to_bf16x2<KF>(vt[h].w[j], false);
-          rw[h][j][1] = bytes2_to_bf16x2<KF>(vt[h].w[j], true);
+          rw[h][j][0] = bytes2_to_bf16x2<KF, false>(vt[h].w[j]);
+          rw[h][j][1] = bytes2_to_bf16x2<KF, true>(vt[h].w[j]);
         }
       }
 #pragma unroll

@@ -6,6 +6,7 @@
 
 namespace pa {
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -34,6 +35,11 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
   return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
 }
 
+// The same rounding with gfx950's packed convert (one instruction for the pair).
+__device__ __forceinline__ uint32_t cvt_bf16x2(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
+}
+
 // Byte permute: result = (hi.half(sel) << 16) | lo.half(sel) for 16-bit halves.
 __device__ __forceinline__ uint32_t pack_lo_halves(uint32_t lo, uint32_t hi) {
   return __builtin_amdgcn_perm(hi, lo, 0x05040100u);
@@ -47,10 +53,6 @@ __device__ __forceinline__ uint32_t pack_hi_halves(uint32_t lo, uint32_t hi) {
 __device__ __forceinline__ f32x2 e4m3x2_lo(uint32_t w) { return __builtin_amdgcn_cvt_pk_f32_fp8(w, false); }
 __device__ __forceinline__ f32x2 e4m3x2_hi(uint32_t w) { return __builtin_amdgcn_cvt_pk_f32_fp8(w, true); }
 
-// Every E4M3 value is exact in bf16, so the bf16 pattern is the upper half of the f32.
-__device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(f32x2 v) {
-  return pack_hi_halves(__float_as_uint(v.x), __float_as_uint(v.y));
-}
 
 // Round a float to E4M3FN: nearest, ties to even, saturating to +-448; NaN keeps its sign.
 __device__ __forceinline__ uint32_t f32_to_e4m3(float y) {

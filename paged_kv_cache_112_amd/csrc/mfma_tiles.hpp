@@ -20,20 +20,30 @@ namespace pa {
 constexpr int kFmtBf16 = 1, kFmtE4m3 = 2, kFmtInt8 = 3;
 constexpr bool byte_fmt(int KF) { return KF != kFmtBf16; }
 
-// Two signed bytes of w (bytes 0, 1 or, with hi, bytes 2, 3) to a bf16 pair.  The
-// bytes are offset to unsigned (x ^ 0x80 = x + 128), converted exactly, and the offset
-// taken back off; |x| <= 128 has at most 8 significant bits, so the bf16 is exact.
-__device__ __forceinline__ uint32_t i8x2_to_bf16x2(uint32_t w, bool hi) {
-  const uint32_t u = (w ^ 0x80808080u) >> (hi ? 16 : 0);
-  const float a = (float)(u & 0xffu) - 128.0f;
-  const float b = (float)((u >> 8) & 0xffu) - 128.0f;
-  return pack_hi_halves(__float_as_uint(a), __float_as_uint(b));
+// Two signed bytes of w (bytes 0, 1, or with HI bytes 2, 3) to a bf16 pair: each byte is
+// sign-extended and converted to f32 exactly (one SDWA convert), and the pair is packed
+// by one convert; |x| <= 128 has at most 8 significant bits, so the bf16 is exact.
+template <bool HI>
+__device__ __forceinline__ uint32_t i8x2_to_bf16x2(uint32_t w) {
+  const int s = (int)w;
+  const float a = HI ? (float)(int8_t)(s >> 16) : (float)(int8_t)s;
+  const float b = HI ? (float)(s >> 24) : (float)(int8_t)(s >> 8);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
 }
 
-template <int KF>
-__device__ __forceinline__ uint32_t bytes2_to_bf16x2(uint32_t w, bool hi) {
-  if constexpr (KF == kFmtInt8) return i8x2_to_bf16x2(w, hi);
-  else return e4m3x2_to_bf16x2(hi ? e4m3x2_hi(w) : e4m3x2_lo(w));
+// Two E4M3 bytes to a bf16 pair: gfx950's packed fp8 -> f32 convert, then the upper
+// halves (every E4M3 value is a bf16 value, so the f32's upper half is exact).  Measured
+// faster than the scaled fp8 -> bf16 convert, which does it in one instruction.
+template <bool HI>
+__device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t w) {
+  const f32x2 v = HI ? e4m3x2_hi(w) : e4m3x2_lo(w);
+  return pack_hi_halves(__float_as_uint(v.x), __float_as_uint(v.y));
+}
+
+template <int KF, bool HI>
+__device__ __forceinline__ uint32_t bytes2_to_bf16x2(uint32_t w) {
+  if constexpr (KF == kFmtInt8) return i8x2_to_bf16x2<HI>(w);
+  else return e4m3x2_to_bf16x2<HI>(w);
 }
 
 template <int KF, int D>
@@ -64,10 +74,10 @@ __device__ __forceinline__ int q_col(int kk, int q4) {
 template <int KF>
 __device__ __forceinline__ bf16x8 bytes8_to_bf16x8(uint32_t w0, uint32_t w1) {
   u32x4 r;
-  r[0] = bytes2_to_bf16x2<KF>(w0, false);
-  r[1] = bytes2_to_bf16x2<KF>(w0, true);
-  r[2] = bytes2_to_bf16x2<KF>(w1, false);
-  r[3] = bytes2_to_bf16x2<KF>(w1, true);
+  r[0] = bytes2_to_bf16x2<KF, false>(w0);
+  r[1] = bytes2_to_bf16x2<KF, true>(w0);
+  r[2] = bytes2_to_bf16x2<KF, false>(w1);
+  r[3] = bytes2_to_bf16x2<KF, true>(w1);
   return __builtin_bit_cast(bf16x8, r);
 }
 
@@ -106,13 +116,13 @@ __device__ __forceinline__ void pv_tile(const VTile<KF, D>& v, uint32_t p01, uin
 #pragma unroll
       for (int c = 0; c < VEC / 2; ++c) rw[j][c] = v.w[j][c];
     } else if constexpr (VEC == 8) {
-      rw[j][0] = bytes2_to_bf16x2<KF>(v.w[j][0], false);
-      rw[j][1] = bytes2_to_bf16x2<KF>(v.w[j][0], true);
-      rw[j][2] = bytes2_to_bf16x2<KF>(v.w[j][1], false);
-      rw[j][3] = bytes2_to_bf16x2<KF>(v.w[j][1], true);
+      rw[j][0] = bytes2_to_bf16x2<KF, false>(v.w[j][0]);
+      rw[j][1] = bytes2_to_bf16x2<KF, true>(v.w[j][0]);
+      rw[j][2] = bytes2_to_bf16x2<KF, false>(v.w[j][1]);
+      rw[j][3] = bytes2_to_bf16x2<KF, true>(v.w[j][1]);
     } else {
-      rw[j][0] = bytes2_to_bf16x2<KF>(v.w[j], false);
-      rw[j][1] = bytes2_to_bf16x2<KF>(v.w[j], true);
+      rw[j][0] = bytes2_to_bf16x2<KF, false>(v.w[j]);
+      rw[j][1] = bytes2_to_bf16x2<KF, true>(v.w[j]);
     }
   }
 #pragma unroll
@@ -141,13 +151,13 @@ __device__ __forceinline__ void pvt_tile(const VTile<KF, D>& v, uint32_t p01, ui
 #pragma unroll
       for (int c = 0; c < VEC / 2; ++c) rw[j][c] = v.w[j][c];
     } else if constexpr (VEC == 8) {
-      rw[j][0] = bytes2_to_bf16x2<KF>(v.w[j][0], false);
-      rw[j][1] = bytes2_to_bf16x2<KF>(v.w[j][0], true);
-      rw[j][2] = bytes2_to_bf16x2<KF>(v.w[j][1], false);
-      rw[j][3] = bytes2_to_bf16x2<KF>(v.w[j][1], true);
+      rw[j][0] = bytes2_to_bf16x2<KF, false>(v.w[j][0]);
+      rw[j][1] = bytes2_to_bf16x2<KF, true>(v.w[j][0]);
+      rw[j][2] = bytes2_to_bf16x2<KF, false>(v.w[j][1]);
+      rw[j][3] = bytes2_to_bf16x2<KF, true>(v.w[j][1]);
     } else {
-      rw[j][0] = bytes2_to_bf16x2<KF>(v.w[j], false);
-      rw[j][1] = bytes2_to_bf16x2<KF>(v.w[j], true);
+      rw[j][0] = bytes2_to_bf16x2<KF, false>(v.w[j]);
+      rw[j][1] = bytes2_to_bf16x2<KF, true>(v.w[j]);
     }
   }
 #pragma unroll
