@@ -62,9 +62,6 @@ __global__ __launch_bounds__(256) void attention_mfma_kernel(const AttnArgs a) {
   constexpr int ESZ = byte_fmt(KF) ? 1 : 2;
   constexpr int VEC = D / 16;
   constexpr int NKK = D / 32;
-  // q^T operands of every wave, in the order the lanes read them (conflict-free)
-  __shared__ u32x4 q_lds[kAttnWaves][NQ][NKK][kWave];
-
   const int kvh = blockIdx.x % a.num_kv_heads;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int i = blockIdx.y;
@@ -93,7 +90,10 @@ __global__ __launch_bounds__(256) void attention_mfma_kernel(const AttnArgs a) {
   const uint32_t qflip = a.qk_scale < 0.f ? 0x80008000u : 0u;
   const bool qzero = a.qk_scale == 0.f;
 
+  // q^T as B operands, kept in registers: group c, lane (n, q4) holds 8 d's of (token
+  // t0 + c*T + tn, head g)
   int qpos[NQ];
+  bf16x8 qreg[NQ][NKK];
 #pragma unroll
   for (int c = 0; c < NQ; ++c) {
     const int tq = t0 + c * T + tn;
@@ -104,7 +104,7 @@ __global__ __launch_bounds__(256) void attention_mfma_kernel(const AttnArgs a) {
     for (int kk = 0; kk < NKK; ++kk) {
       u32x4 w = {0u, 0u, 0u, 0u};
       if (tq < nq && !qzero) w = ld16(qrow + q_col<KF, D>(kk, q4)) ^ qflip;
-      q_lds[wave][c][kk][lane] = w;
+      qreg[c][kk] = __builtin_bit_cast(bf16x8, w);
     }
   }
 
@@ -134,20 +134,26 @@ __global__ __launch_bounds__(256) void attention_mfma_kernel(const AttnArgs a) {
   // K or V tiles of step st (keys 32*st .. 32*st + 31).  With blocks of 16 tokens or
   // more, a step inside the context has each of its two tiles in one block at a uniform
   // offset, the same for K and V: scalar base plus the per-lane constant offsets.
+  // The block ids of a step are read one step before its addresses are formed (at the
+  // end of the step before that), so the scalar loads are not waited on.
   struct StepAddr {
     int64_t off[2];
     bool fast;
   };
-  auto step_addr = [&](int st) {
+  auto step_fast = [&](int st) { return __builtin_expect(BIGBS && 32 * st + 32 <= S, 1); };
+  auto load_ids = [&](int st, int32_t (&id)[2]) {
+    if (step_fast(st)) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) id[h] = attn_load_uniform(bt_row + ((32 * st + 16 * h) >> a.log2_bs));
+    }
+  };
+  auto step_addr = [&](int st, const int32_t (&id)[2]) {
     StepAddr t;
-    t.fast = BIGBS && 32 * st + 32 <= S;
+    t.fast = step_fast(st);
     if (t.fast) {
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int key = 32 * st + 16 * h;
-        const int32_t blk = attn_load_uniform(bt_row + (key >> a.log2_bs));
-        t.off[h] = (int64_t)blk * a.block_bytes + (int64_t)((uint32_t)(key & bs_mask) * row_bytes);
-      }
+      for (int h = 0; h < 2; ++h)
+        t.off[h] = (int64_t)id[h] * a.block_bytes + (int64_t)((uint32_t)((32 * st + 16 * h) & bs_mask) * row_bytes);
     }
     return t;
   };
@@ -210,18 +216,13 @@ __global__ __launch_bounds__(256) void attention_mfma_kernel(const AttnArgs a) {
         }
       }
     }
-    // The q operands are read from LDS at each step (an empty asm makes their address
-    // opaque, so they are not hoisted out of the loop into registers).
-    const __attribute__((address_space(3))) u32x4* qw =
-        (const __attribute__((address_space(3))) u32x4*)&q_lds[wave][0][0][lane];
-    asm volatile("" : "+v"(qw));
     // q.K^T of group c: s[h] register r = score of key 32*st + 16*h + 4*q4 + r, column n
     auto qk = [&](int c, f32x4 (&s)[2]) {
       s[0] = f32x4{0.f, 0.f, 0.f, 0.f};
       s[1] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk) {
-        const bf16x8 qb = __builtin_bit_cast(bf16x8, qw[(c * NKK + kk) * kWave]);
+        const bf16x8 qb = qreg[c][kk];
         s[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[0][kk], qb, s[0], 0, 0, 0);
         s[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[1][kk], qb, s[1], 0, 0, 0);
       }
@@ -246,7 +247,7 @@ __global__ __launch_bounds__(256) void attention_mfma_kernel(const AttnArgs a) {
       for (int h = 0; h < 2; ++h)
 #pragma unroll
         for (int r = 0; r < 4; ++r) grow |= s[h][r] > thr[c];
-      if (__builtin_amdgcn_ballot_w64(grow) != 0) {   // uniform: raise this group's references
+      if (__builtin_expect(__builtin_amdgcn_ballot_w64(grow) != 0, 0)) {   // uniform, rare: raise the references
         const float v = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
                               fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
         const float mn = fmaxf(m[c], col_max(v) * sc);
@@ -305,18 +306,23 @@ __global__ __launch_bounds__(256) void attention_mfma_kernel(const AttnArgs a) {
   // clamped rows.  Steps that every column sees whole run without the mask.
   KTile<KF, D> k[2];
   VTile<KF, D> v[2];
+  int32_t ids[2] = {0, 0};   // block ids of the tiles of the next step
   auto step = [&](auto masked_tag, int st) {
-    const StepAddr next = step_addr(st + 1);
+    const StepAddr next = step_addr(st + 1, ids);
     bf16x8 pB[NQ];
     scores(masked_tag, k, st, pB);
     load_k(k, st + 1, next);
     accumulate(v, pB);
     load_v(v, st + 1, next);
+    load_ids(st + 2, ids);
   };
   {
-    const StepAddr first = step_addr(0);
+    int32_t id0[2] = {0, 0};
+    load_ids(0, id0);
+    const StepAddr first = step_addr(0, id0);
     load_k(k, 0, first);
     load_v(v, 0, first);
+    load_ids(1, ids);
   }
   int st = 0;
   for (; st < nfull; ++st) step(std::false_type{}, st);
