@@ -34,34 +34,51 @@ __global__ __launch_bounds__(64) void merge_kernel(const MergeArgs a) {
   const float* ls = a.ws_l + r0;
   const float* os = a.ws_o + r0 * D + d0;   // os[j * H * D]
 
-  float M = -INFINITY;
-  for (int j = lane; j < n; j += kWave) M = fmaxf(M, ms[j * H]);
+  // Every load of the first round (16 partitions, all of them for n <= 16) is issued
+  // before the maxima are formed: the pieces do not depend on them, so the wave waits
+  // for one memory round trip.  Lane j holds m_j and l_j (n <= 64; beyond, the
+  // weights are read again from memory).
+  f32x4 ov[4][DPL / 4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int jc = min(4 * u + pg, n - 1);
+#pragma unroll
+    for (int c = 0; c < DPL / 4; ++c) ov[u][c] = __builtin_bit_cast(f32x4, ld16(os + jc * H * D + 4 * c));
+  }
+  const float m_lane = lane < n ? ms[lane * H] : -INFINITY;
+  const float l_lane = lane < n ? ls[lane * H] : 0.f;
+  float M = m_lane;
+  for (int j = lane + kWave; j < n; j += kWave) M = fmaxf(M, ms[j * H]);
   M = wave_max(M);
-  float L = 0.f;
-  for (int j = lane; j < n; j += kWave) L += ls[j * H] * __builtin_amdgcn_exp2f(ms[j * H] - M);
+  float L = lane < n ? l_lane * __builtin_amdgcn_exp2f(m_lane - M) : 0.f;
+  for (int j = lane + kWave; j < n; j += kWave) L += ls[j * H] * __builtin_amdgcn_exp2f(ms[j * H] - M);
   L = wave_sum(L);
+  auto weight = [&](int j) -> float {   // 2^(m_j - M), 0 past the last partition
+    const int jc = min(j, n - 1);
+    const float mj = n <= kWave ? __shfl(m_lane, jc) : ms[jc * H];   // every lane takes part
+    return j < n ? __builtin_amdgcn_exp2f(mj - M) : 0.f;
+  };
 
-  // four partitions per wave load; all loads of a round of 16 partitions are issued together
   float acc[DPL];
 #pragma unroll
   for (int i = 0; i < DPL; ++i) acc[i] = 0.f;
-  for (int j0 = 0; j0 < n; j0 += 16) {
-    f32x4 ov[4][DPL / 4];
-    float wv[4];
+  for (int j0 = 0;;) {
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const int j = j0 + 4 * u + pg;
-      const int jc = min(j, n - 1);
-      wv[u] = j < n ? __builtin_amdgcn_exp2f(ms[jc * H] - M) : 0.f;
-#pragma unroll
-      for (int c = 0; c < DPL / 4; ++c) ov[u][c] = __builtin_bit_cast(f32x4, ld16(os + jc * H * D + 4 * c));
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
+      const float wv = weight(j0 + 4 * u + pg);
 #pragma unroll
       for (int c = 0; c < DPL / 4; ++c)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) acc[4 * c + e] = fmaf(wv[u], ov[u][c][e], acc[4 * c + e]);
+        for (int e = 0; e < 4; ++e) acc[4 * c + e] = fmaf(wv, ov[u][c][e], acc[4 * c + e]);
+    }
+    j0 += 16;
+    if (j0 >= n) break;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int jc = min(j0 + 4 * u + pg, n - 1);
+#pragma unroll
+      for (int c = 0; c < DPL / 4; ++c) ov[u][c] = __builtin_bit_cast(f32x4, ld16(os + jc * H * D + 4 * c));
+    }
   }
 #pragma unroll
   for (int i = 0; i < DPL; ++i) {
