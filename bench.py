@@ -118,6 +118,70 @@ def _time_launches(torch, fn, reps, warmup):
     return e0.elapsed_time(e1) * 1e3 / reps
 
 
+# A plain streaming read, the practical ceiling the decode's HBM figure is set against:
+# each thread reads 16 bytes per step of a grid-stride loop and XOR-folds them into one
+# word it stores.  Built with hipcc when --op stream_read asks for it (not part of the
+# library, not in the default run).
+STREAM_READ_SRC = r"""
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+__global__ __launch_bounds__(256) void stream_read(const u32x4* __restrict__ p, size_t n16, uint32_t* out) {
+  size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  const size_t stride = (size_t)gridDim.x * 256;
+  uint32_t x = 0;
+  for (; i < n16; i += stride) {
+    const u32x4 v = p[i];
+    x ^= v[0] ^ v[1] ^ v[2] ^ v[3];
+  }
+  out[(size_t)blockIdx.x * 256 + threadIdx.x] = x;
+}
+extern "C" int stream_read_launch(const void* p, size_t bytes, void* out, int grid, void* stream) {
+  hipLaunchKernelGGL(stream_read, dim3(grid), dim3(256), 0, (hipStream_t)stream, (const u32x4*)p, bytes / 16,
+                     (uint32_t*)out);
+  return (int)hipGetLastError();
+}
+"""
+
+
+def bench_stream_read(args, torch):
+    """Best GB/s of a plain streaming read over the decode's byte count and over 2 GiB."""
+    import ctypes
+    import subprocess
+    import tempfile
+    from paged_kv_cache_112_amd.build import ARCH, hipcc
+    tmp = tempfile.mkdtemp(prefix="pa_stream_read_")
+    src, lib = os.path.join(tmp, "stream_read.hip"), os.path.join(tmp, "stream_read.so")
+    with open(src, "w") as f:
+        f.write(STREAM_READ_SRC)
+    subprocess.run([hipcc(), f"--offload-arch={ARCH}", "-O3", "-shared", "-fPIC", "-Xclang", "-target-feature",
+                    "-Xclang", "-packed-fp32-ops", "-o", lib, src], check=True, capture_output=True)
+    L = ctypes.CDLL(lib)
+    L.stream_read_launch.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+    dev = torch.device("cuda:0")
+    from workloads import make_config
+    w = make_config(WORKLOAD)
+    decode_bytes = algorithmic_bytes(w)["partition"] // 16 * 16
+    buf = torch.ones((2 << 30) // 4, dtype=torch.int32, device=dev)
+    grids = (512, 1024, 2048, 4096)
+    out = torch.empty(max(grids) * 256, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream().cuda_stream
+    results = []
+    for nbytes in (decode_bytes, 2 << 30):
+        best = None
+        for grid in grids:
+            us = _time_launches(torch, lambda: L.stream_read_launch(buf.data_ptr(), nbytes, out.data_ptr(), grid, stream),
+                                max(args.steps, 10), max(args.warmup, 3))
+            gbs = nbytes / us / 1e3
+            if best is None or gbs > best[1]:
+                best = (grid, gbs, us)
+        results.append({"bytes": nbytes, "best_grid": best[0], "us": round(best[2], 2), "GB/s": round(best[1], 1),
+                        "frac_of_8TBps": round(best[1] / 8000.0, 4)})
+    print(json.dumps({"metric": "plain streaming read (reference ceiling for the decode's HBM figure)",
+                      "results": results, "timing": "HIP events around back-to-back launches, best of grids " +
+                      str(list(grids))}))
+
+
 def side_op(args, w, torch, pa):
     """One JSON line for a measurement beside the headline step (not the default bench line)."""
     dev = torch.device("cuda:0")
@@ -293,11 +357,12 @@ def main():
     ap.add_argument("--copy-calibrate", type=int, default=0, metavar="MIB",
                     help="only copy MIB MiB with torch (a plain copy of known size, for counter scaling)")
     ap.add_argument("--op", default="decode",
-                    choices=["decode", "copy_blocks", "write_prefill", "attention", "graph_loop"],
+                    choices=["decode", "copy_blocks", "write_prefill", "attention", "graph_loop", "stream_read"],
                     help="decode: the hot-path step (the headline line); copy_blocks: copy-on-write block "
                          "copies over the workload's pools; write_prefill: pa_write_kv of every context token; "
                          "attention: multi-query paged attention on llama3_8b_chunk512; graph_loop: the decode "
-                         "loop with device-side slot mapping, captured once and replayed")
+                         "loop with device-side slot mapping, captured once and replayed; stream_read: a plain "
+                         "streaming read of the same byte count, the practical HBM ceiling")
     ap.add_argument("--contiguous", action="store_true",
                     help="identity-ordered block tables (each sequence's blocks adjacent): the contiguous comparator")
     args = ap.parse_args()
@@ -325,6 +390,8 @@ def main():
         build()
     if args.op == "attention":
         return bench_attention(args, torch, pa)
+    if args.op == "stream_read":
+        return bench_stream_read(args, torch)
     if args.op == "graph_loop":
         return bench_graph_loop(args, torch, pa)
     dev = torch.device("cuda:0")
