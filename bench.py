@@ -249,8 +249,24 @@ def bench_attention(args, torch, pa):
     shape = (w.num_blocks, w.block_size, w.num_kv_heads, w.head_dim)
     gen = torch.Generator(device=dev)
     gen.manual_seed(w.seed)
-    pools = [(torch.randn(shape, generator=gen, device=dev).to(torch.bfloat16),
-              torch.randn(shape, generator=gen, device=dev).to(torch.bfloat16)) for _ in range(LAYERS)]
+    kvd = args.kv_dtype or "bf16"
+    esz = 1 if kvd in ("e4m3", "i8") else 2
+    k_scale = v_scale = 1.0
+
+    def pool():
+        x = torch.randn(shape, generator=gen, device=dev)
+        if kvd == "bf16":
+            return x.to(torch.bfloat16)
+        # random codes of the one-byte format: e4m3 codes with the NaN patterns cleared, int8 in [-127, 127]
+        if kvd == "e4m3":
+            c = torch.randint(0, 256, shape, generator=gen, device=dev, dtype=torch.int32)
+            c = torch.where((c & 0x7F) == 0x7F, c - 1, c)
+            return c.to(torch.uint8)
+        return torch.randint(-127, 128, shape, generator=gen, device=dev, dtype=torch.int32).to(torch.int8)
+
+    if kvd in ("e4m3", "i8"):
+        k_scale = v_scale = 0.01
+    pools = [(pool(), pool()) for _ in range(LAYERS)]
     qsl = w.query_start_loc()
     n = int(qsl[-1])
     q = torch.randn((n, w.num_q_heads, w.head_dim), generator=gen, device=dev).to(torch.bfloat16)
@@ -264,17 +280,17 @@ def bench_attention(args, torch, pa):
     def call():
         kc, vc = pools[turn[0] % LAYERS]
         turn[0] += 1
-        pa.paged_attention(q, kc, vc, bt, sl, qs, w.scale, maxq, out=out)
+        pa.paged_attention(q, kc, vc, bt, sl, qs, w.scale, maxq, out=out, k_scale=k_scale, v_scale=v_scale)
 
     us = _time_launches(torch, call, max(args.steps, 10), max(args.warmup, 3))
     # causal work actually needed: new token j of sequence b sees p + 1 keys, p = S - n + j
     keys = sum(int(S) * int(nq) - int(nq) * (int(nq) - 1) // 2 for S, nq in zip(w.context_lens, w.query_lens))
     flops = 4 * w.head_dim * w.num_q_heads * keys
-    kv_bytes = int(w.context_lens.sum()) * w.num_kv_heads * w.head_dim * 2 * 2
+    kv_bytes = int(w.context_lens.sum()) * w.num_kv_heads * w.head_dim * 2 * esz
     qo_bytes = 2 * n * w.num_q_heads * w.head_dim * 2
     tflops = flops / us / 1e6
     print(json.dumps({"metric": "pa_paged_attention (multi-query, causal), llama3_8b_chunk512",
-                      "workload": w.name, "new_tokens": n, "us_per_call": round(us, 2),
+                      "workload": w.name, "kv_dtype": kvd, "new_tokens": n, "us_per_call": round(us, 2),
                       "TFLOP/s": round(tflops, 1), "frac_of_bf16_mfma_2.5PF": round(tflops / 2500.0, 4),
                       "unique_kv_and_qo_bytes": kv_bytes + qo_bytes,
                       "GB/s_unique": round((kv_bytes + qo_bytes) / us / 1e3, 1),

@@ -146,24 +146,37 @@ def test_sequences_with_no_new_tokens_and_bad_lengths_are_skipped():
     assert np.abs(got[:4] - ref[:4]).max() <= 2e-2
 
 
-def test_chunk512_full_size_sampled_rows():
-    """llama3_8b_chunk512 at full size; every row of three sequences and spread rows of all, vs the oracle."""
+@pytest.mark.parametrize("kv", ["bf16", "e4m3", "i8"])
+def test_chunk512_full_size_sampled_rows(kv):
+    """llama3_8b_chunk512 at full size; every row of three sequences and spread rows of all, vs the oracle.
+    One-byte pools hold uniformly drawn codes (e4m3 NaN codes excluded) with scale 0.01."""
     import torch
     import paged_kv_cache_112_amd as pa
     w = make_mq_config("llama3_8b_chunk512")
     rng = np.random.default_rng(w.seed)
     shape = (w.num_blocks, w.block_size, w.num_kv_heads, w.head_dim)
-    kc = f32_to_bf16_bits(rng.standard_normal(shape).astype(np.float32))
-    vc = f32_to_bf16_bits(rng.standard_normal(shape).astype(np.float32))
+    ks = vs = 1.0
+    if kv == "bf16":
+        kc = f32_to_bf16_bits(rng.standard_normal(shape).astype(np.float32))
+        vc = f32_to_bf16_bits(rng.standard_normal(shape).astype(np.float32))
+    elif kv == "e4m3":
+        kc, vc = (rng.integers(0, 256, shape, dtype=np.uint8) for _ in range(2))
+        for c in (kc, vc):
+            c[(c & 0x7F) == 0x7F] -= 1
+        ks = vs = 0.01
+    else:
+        kc, vc = (rng.integers(-127, 128, shape).astype(np.int8) for _ in range(2))
+        ks = vs = 0.01
     q = f32_to_bf16_bits(w.mq_q_values())
     qsl = w.query_start_loc()
     out = pa.paged_attention(to_dev(q), to_dev(kc), to_dev(vc), to_dev(w.block_tables), to_dev(w.context_lens),
-                             to_dev(qsl), w.scale, int(w.query_lens.max()))
+                             to_dev(qsl), w.scale, int(w.query_lens.max()), k_scale=ks, v_scale=vs)
     torch.cuda.synchronize()
     got = out_to_f64(out)
     rows = set(range(int(qsl[0]), int(qsl[0]) + 8)) | set(range(int(qsl[16]) + 500, int(qsl[17])))
     rows |= set(int(r) for r in rng.choice(int(qsl[-1]), 40, replace=False))
     rows |= {int(qsl[b + 1]) - 1 for b in range(w.num_seqs)}          # each sequence's last row
-    ref = oracle.paged_attention(q, kc, vc, w.block_tables, w.context_lens, qsl, w.scale, "bf16", "bf16", rows=rows)
+    ref = oracle.paged_attention(q, kc, vc, w.block_tables, w.context_lens, qsl, w.scale, kv, "bf16", ks, vs,
+                                 rows=rows)
     idx = sorted(rows)
     assert np.abs(got[idx] - ref[idx]).max() <= 2e-2
