@@ -4,7 +4,9 @@ Workload: one Llama-3-8B attention layer (32 query heads, 8 KV heads, head dim
 128, bf16), batch 64, block size 16, context lengths = prompt U[100,2000] +
 output U[20,1500] from the seeded generator, physical blocks shuffled over a
 pool 10 % larger than needed.  One step is the whole hot path for one batch:
-pa_write_kv of this step's 64 tokens, then pa_decode (partition kernel + merge).
+pa_write_kv of this step's 64 tokens, then pa_decode (partition kernel + merge);
+with --fused the partition kernel writes the tokens itself
+(pa_decode_partition_append).
 Each step uses the next of L layer-pool copies, as a model's layers would, so
 the 256 MB MALL cannot serve a pool read by an earlier step.
 
@@ -47,9 +49,10 @@ def algorithmic_bytes(w, kv_bytes=2, q_bytes=2, out_bytes=2, in_bytes=2):
     q = w.num_seqs * w.num_q_heads * w.head_dim * q_bytes
     out = w.num_seqs * w.num_q_heads * w.head_dim * out_bytes
     tables = 4 * int(((ctx + w.block_size - 1) // w.block_size).sum()) + 4 * w.num_seqs
-    write = w.num_seqs * w.num_kv_heads * w.head_dim * 2 * (in_bytes + kv_bytes) + 4 * w.num_seqs
-    return {"partition": kv + q + tables, "decode": kv + q + out + tables, "write": write,
-            "step": kv + q + out + tables + write, "kv": kv}
+    rows = w.num_seqs * w.num_kv_heads * w.head_dim * 2 * (in_bytes + kv_bytes)
+    write = rows + 4 * w.num_seqs
+    return {"partition": kv + q + tables, "partition_append": kv + q + tables + rows, "decode": kv + q + out + tables,
+            "write": write, "step": kv + q + out + tables + write, "kv": kv}
 
 
 def kernel_sha() -> str:
@@ -379,6 +382,9 @@ def main():
                          "attention: multi-query paged attention on llama3_8b_chunk512; graph_loop: the decode "
                          "loop with device-side slot mapping, captured once and replayed; stream_read: a plain "
                          "streaming read of the same byte count, the practical HBM ceiling")
+    ap.add_argument("--fused", action="store_true",
+                    help="the step's write done by the partition launch itself (pa_decode_partition_append + "
+                         "pa_merge) instead of pa_write_kv + pa_decode_partition + pa_merge")
     ap.add_argument("--contiguous", action="store_true",
                     help="identity-ordered block tables (each sequence's blocks adjacent): the contiguous comparator")
     args = ap.parse_args()
@@ -467,15 +473,27 @@ def main():
 
     stream = torch.cuda.current_stream()
 
+    # --fused: the step's write is done by the partition launch itself (matrix-core grid
+    # kernel, partitions of 256 tokens or more)
+    fused = args.fused and args.kernel in (0, 2) and P >= 256 and w.kv_dtype != "f32"
+
+    def partition(kc, vc):
+        if fused:
+            pa.decode_partition_append(q, k_new, v_new, kc, vc, bt, ctx, w.scale, out=out, max_context_len=max_ctx,
+                                       workspace=ws, partition_tokens=P, k_scale=k_scale, v_scale=v_scale)
+        else:
+            pa.decode_partition(q, kc, vc, bt, ctx, w.scale, out=out, max_context_len=max_ctx, workspace=ws,
+                                partition_tokens=P, kernel=args.kernel, k_scale=k_scale, v_scale=v_scale)
+
     def step(i, ev=None):
         kc, vc = pools[i % LAYERS]
         if ev is not None:
             ev[0].record(stream)
-        pa.write_kv(k_new, v_new, slots, kc, vc, k_scale, v_scale)
+        if not fused:
+            pa.write_kv(k_new, v_new, slots, kc, vc, k_scale, v_scale)
         if ev is not None:
             ev[1].record(stream)
-        pa.decode_partition(q, kc, vc, bt, ctx, w.scale, out=out, max_context_len=max_ctx, workspace=ws,
-                            partition_tokens=P, kernel=args.kernel, k_scale=k_scale, v_scale=v_scale)
+        partition(kc, vc)
         if ev is not None:
             ev[2].record(stream)
         pa.merge(ws, ctx, out, max_ctx, P)
@@ -529,10 +547,7 @@ def main():
     with torch.cuda.stream(side):
         with torch.cuda.graph(part_graph, stream=side):
             for i in range(LAYERS):
-                kc, vc = pools[i]
-                pa.decode_partition(q, kc, vc, bt, ctx, w.scale, out=out, max_context_len=max_ctx,
-                                    workspace=ws, partition_tokens=P, kernel=args.kernel, k_scale=k_scale,
-                                    v_scale=v_scale)
+                partition(*pools[i])
     stream.wait_stream(side)
     torch.cuda.synchronize()
     reps = max(1, args.steps // LAYERS)
@@ -562,9 +577,10 @@ def main():
 
     nb = algorithmic_bytes(w, kv_bytes=1 if fp8 else 2)
     value = nb["step"] / (ms_per_step * 1e-3) / 1e9
-    achieved = nb["partition"] / (part_launch_ms * 1e-3) / 1e9
+    launch_bytes = nb["partition_append"] if fused else nb["partition"]
+    achieved = launch_bytes / (part_launch_ms * 1e-3) / 1e9
     # the committed counter run covers the default launch of the headline workload only
-    default_launch = (w.name == WORKLOAD and P == 256 and args.kernel in (0, 2) and not args.contiguous)
+    default_launch = (w.name == WORKLOAD and P == 256 and args.kernel in (0, 2) and not args.contiguous and not fused)
     traffic = measured_traffic() if default_launch else None
     result = {
         "metric": "paged-attn decode achieved HBM GB/s + tokens/s, Llama-3-8B layer, batch 64",
@@ -584,9 +600,12 @@ def main():
         "config": {"workload": w.name, "batch": B, "num_q_heads": hq, "num_kv_heads": hkv, "head_dim": d,
                    "block_size": bs, "sum_context": w.total_tokens, "max_context": max_ctx,
                    "partition_tokens": P, "kernel": ["auto", "valu", "mfma", "mfma_persist"][args.kernel],
-                   "layer_pools_rotated": LAYERS, "step": "pa_write_kv(64 tokens) + pa_decode",
+                   "layer_pools_rotated": LAYERS,
+                   "step": ("pa_decode_partition_append (writes the 64 new tokens, then decodes) + pa_merge"
+                            if fused else "pa_write_kv(64 tokens) + pa_decode_partition + pa_merge"),
                    "block_order": "identity (contiguous comparator)" if args.contiguous else "seeded permutation"},
-        "kernel_us": {"write_kv": round(write_ms * 1e3, 2), "decode_partition": round(part_ms * 1e3, 2),
+        "kernel_us": {"write_kv": round(write_ms * 1e3, 2) if not fused else 0.0,
+                      "decode_partition": round(part_ms * 1e3, 2),
                       "merge": round(merge_ms * 1e3, 2)},
         "decode_partition_us_back_to_back": round(part_launch_ms * 1e3, 2),
         "timing": "steps replayed from a HIP graph of the 8 layer steps; kernel_us: HIP events around each "
@@ -594,8 +613,10 @@ def main():
                   "around back-to-back replays of the partition kernel alone",
         "eager_ms_per_step": round(eager_ms, 5) if eager_ms else None,
         "bytes": nb,
-        "roofline": {"bound": "hbm", "kernel": "decode_mfma_kernel (partition stage)",
-                     "bytes_per_launch": nb["partition"],
+        "roofline": {"bound": "hbm",
+                     "kernel": ("decode_mfma_kernel (partition stage, appending the step's tokens)" if fused
+                                else "decode_mfma_kernel (partition stage)"),
+                     "bytes_per_launch": launch_bytes,
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic},
     }

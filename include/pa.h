@@ -220,6 +220,40 @@ pa_status pa_decode_partition(const void* q, int32_t q_dtype, int32_t num_seqs, 
                               void* out, void* workspace, size_t workspace_bytes,
                               int32_t partition_tokens, int32_t kernel, void* stream);
 
+/* pa_write_kv of this step's tokens and pa_decode in one partition launch (plus the
+ * merge), for the decode step where every sequence appends one token.  For each
+ * sequence b with ctx = context_lens[b] >= 1 (the length after the append), the
+ * rows k_new[b], v_new[b] are stored at position ctx - 1, i.e. at
+ *   slot = block_tables[b, (ctx - 1) / block_size] * block_size + (ctx - 1) % block_size
+ * (the slot mapping of ai-infra-handbooks "Paged KV cache", "Block tables and slot
+ * mapping"), in the pool's format exactly as pa_write_kv would store them,
+ * and then attends over positions 0 .. ctx - 1 as pa_decode does.  The workgroup
+ * whose partition holds position ctx - 1 writes the rows and waits for the stores
+ * before it reads any row, so the results, and the pools afterwards, are bit for bit
+ * those of pa_write_kv followed by pa_decode.  A sequence with ctx == 0 appends
+ * nothing and gets zeros.
+ *   k_new, v_new  device [num_seqs, num_kv_heads, head_dim], in_dtype PA_BF16
+ *   k_cache, v_cache  the pools, written at the appended slots and read
+ *   partition_tokens  256, 512 or 1024 (0 = the default, 256)
+ *   the other arguments as pa_decode; the matrix-core grid kernel runs (bf16 q with
+ *   a bf16, e4m3 or int8 pool, query-head group <= 16).
+ * Errors: as pa_decode; PA_ERR_NULL for a null k_new or v_new; PA_ERR_DTYPE for
+ * another in_dtype; PA_ERR_UNSUPPORTED for an f32 pool or a partition below 256. */
+pa_status pa_decode_append(const void* q, int32_t q_dtype, const void* k_new, const void* v_new, int32_t in_dtype,
+                           int32_t num_seqs, int32_t num_q_heads, void* k_cache, void* v_cache,
+                           const pa_kv_cache* cache, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                           const int32_t* context_lens, int32_t max_context_len, float scale, void* out,
+                           void* workspace, size_t workspace_bytes, int32_t partition_tokens, void* stream);
+
+/* First stage of pa_decode_append alone (same arguments and checks; the pieces and
+ * outputs as pa_decode_partition). */
+pa_status pa_decode_partition_append(const void* q, int32_t q_dtype, const void* k_new, const void* v_new,
+                                     int32_t in_dtype, int32_t num_seqs, int32_t num_q_heads, void* k_cache,
+                                     void* v_cache, const pa_kv_cache* cache, const int32_t* block_tables,
+                                     int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                     int32_t max_context_len, float scale, void* out, void* workspace,
+                                     size_t workspace_bytes, int32_t partition_tokens, void* stream);
+
 /* Second stage of pa_decode: for every sequence with n = ceil(context_lens[b] / P)
  * >= 2 partitions and every query head,
  *   out = sum_j 2^(m_j - M) o_j / sum_j 2^(m_j - M) l_j,   M = max_j m_j,

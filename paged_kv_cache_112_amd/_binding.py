@@ -21,6 +21,7 @@ PA_F32, PA_BF16, PA_FP8_E4M3, PA_INT8 = 0, 1, 2, 3
 PA_KERNEL_AUTO, PA_KERNEL_VALU, PA_KERNEL_MFMA, PA_KERNEL_MFMA_PERSIST = 0, 1, 2, 3
 
 EXPORTED = ("pa_write_kv", "pa_copy_blocks", "pa_copy_blocks_layers", "pa_paged_attention", "pa_slot_mapping", "pa_decode", "pa_decode_partition", "pa_merge",
+            "pa_decode_append", "pa_decode_partition_append",
             "pa_decode_workspace_bytes", "pa_default_partition_tokens", "pa_status_str")
 
 
@@ -41,6 +42,8 @@ _lib = None
 _vp, _i32, _i64, _f32, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
 _DECODE_ARGS = [_vp, _i32, _i32, _i32, _vp, _vp, ctypes.POINTER(PaKvCache), _vp, _i32, _vp, _i32, _f32,
                 _vp, _vp, _sz, _i32, _i32, _vp]
+_APPEND_ARGS = [_vp, _i32, _vp, _vp, _i32, _i32, _i32, _vp, _vp, ctypes.POINTER(PaKvCache), _vp, _i32, _vp, _i32,
+                _f32, _vp, _vp, _sz, _i32, _vp]
 
 
 def lib() -> ctypes.CDLL:
@@ -66,6 +69,10 @@ def lib() -> ctypes.CDLL:
         L.pa_decode.restype = ctypes.c_int
         L.pa_decode_partition.argtypes = _DECODE_ARGS
         L.pa_decode_partition.restype = ctypes.c_int
+        L.pa_decode_append.argtypes = _APPEND_ARGS
+        L.pa_decode_append.restype = ctypes.c_int
+        L.pa_decode_partition_append.argtypes = _APPEND_ARGS
+        L.pa_decode_partition_append.restype = ctypes.c_int
         L.pa_merge.argtypes = [_vp, _sz, _i32, _i32, _i32, _vp, _i32, _i32, _i32, _vp, _vp]
         L.pa_merge.restype = ctypes.c_int
         L.pa_decode_workspace_bytes.argtypes = [_i32, _i32, _i32, _i32, _i32]
@@ -131,6 +138,23 @@ def pa_decode_partition(q, q_dtype, num_seqs, num_q_heads, k_cache, v_cache, cac
     return lib().pa_decode_partition(q, q_dtype, num_seqs, num_q_heads, k_cache, v_cache, ctypes.byref(cache),
                                      block_tables, max_blocks_per_seq, context_lens, max_context_len, scale, out,
                                      workspace, workspace_bytes, partition_tokens, kernel, stream)
+
+
+def pa_decode_append(q, q_dtype, k_new, v_new, in_dtype, num_seqs, num_q_heads, k_cache, v_cache, cache: PaKvCache,
+                     block_tables, max_blocks_per_seq, context_lens, max_context_len, scale, out, workspace,
+                     workspace_bytes, partition_tokens=0, stream=None) -> int:
+    return lib().pa_decode_append(q, q_dtype, k_new, v_new, in_dtype, num_seqs, num_q_heads, k_cache, v_cache,
+                                  ctypes.byref(cache), block_tables, max_blocks_per_seq, context_lens,
+                                  max_context_len, scale, out, workspace, workspace_bytes, partition_tokens, stream)
+
+
+def pa_decode_partition_append(q, q_dtype, k_new, v_new, in_dtype, num_seqs, num_q_heads, k_cache, v_cache,
+                               cache: PaKvCache, block_tables, max_blocks_per_seq, context_lens, max_context_len,
+                               scale, out, workspace, workspace_bytes, partition_tokens=0, stream=None) -> int:
+    return lib().pa_decode_partition_append(q, q_dtype, k_new, v_new, in_dtype, num_seqs, num_q_heads, k_cache,
+                                            v_cache, ctypes.byref(cache), block_tables, max_blocks_per_seq,
+                                            context_lens, max_context_len, scale, out, workspace, workspace_bytes,
+                                            partition_tokens, stream)
 
 
 def pa_merge(workspace, workspace_bytes, num_seqs, num_q_heads, head_dim, context_lens, max_context_len,
@@ -310,6 +334,49 @@ def decode_partition(q, k_cache, v_cache, block_tables, context_lens, scale, out
     """pa_decode_partition on torch tensors; returns (out, workspace)."""
     return _decode_common(pa_decode_partition, q, k_cache, v_cache, block_tables, context_lens, scale, out,
                           max_context_len, workspace, partition_tokens, kernel, k_scale, v_scale, stream)
+
+
+def _append_common(fn, q, k_new, v_new, k_cache, v_cache, block_tables, context_lens, scale, out, max_context_len,
+                   workspace, partition_tokens, k_scale, v_scale, stream):
+    torch = _torch()
+    B, hq, d = q.shape
+    if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
+        raise ValueError("block_tables and context_lens must be int32")
+    if block_tables.dim() != 2 or block_tables.shape[0] != B or context_lens.numel() != B:
+        raise ValueError("block_tables [B, max_blocks] and context_lens [B] must match q")
+    if k_cache.shape != v_cache.shape or k_cache.shape[3] != d:
+        raise ValueError("pools must match each other and q's head_dim")
+    if k_new.shape != v_new.shape or tuple(k_new.shape) != (B, k_cache.shape[2], d):
+        raise ValueError("k_new, v_new must be [B, H_kv, head_dim]")
+    if max_context_len is None:
+        max_context_len = block_tables.shape[1] * k_cache.shape[1]
+    if out is None:
+        out = torch.empty_like(q)
+    if workspace is None:
+        workspace = new_workspace(B, hq, d, max_context_len, partition_tokens, q.device)
+    ws_ptr = _ptr(workspace) if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    desc = cache_desc(k_cache, k_scale, v_scale)
+    check(fn(_ptr(q), dtype_code(q), _ptr(k_new), _ptr(v_new), dtype_code(k_new), B, hq, _ptr(k_cache),
+             _ptr(v_cache), desc, _ptr(block_tables), block_tables.shape[1], _ptr(context_lens), int(max_context_len),
+             float(scale), _ptr(out), ws_ptr, ws_bytes, int(partition_tokens), _stream(stream)))
+    return out, workspace
+
+
+def decode_append(q, k_new, v_new, k_cache, v_cache, block_tables, context_lens, scale, out=None,
+                  max_context_len=None, workspace=None, partition_tokens=0, k_scale=1.0, v_scale=1.0, stream=None):
+    """pa_decode_append on torch tensors: k_new, v_new [B, H_kv, d] bf16 are stored at position
+    context_lens[b] - 1 and the decode runs over positions 0 .. context_lens[b] - 1; returns ``out``."""
+    return _append_common(pa_decode_append, q, k_new, v_new, k_cache, v_cache, block_tables, context_lens, scale,
+                          out, max_context_len, workspace, partition_tokens, k_scale, v_scale, stream)[0]
+
+
+def decode_partition_append(q, k_new, v_new, k_cache, v_cache, block_tables, context_lens, scale, out=None,
+                            max_context_len=None, workspace=None, partition_tokens=0, k_scale=1.0, v_scale=1.0,
+                            stream=None):
+    """pa_decode_partition_append on torch tensors; returns (out, workspace)."""
+    return _append_common(pa_decode_partition_append, q, k_new, v_new, k_cache, v_cache, block_tables, context_lens,
+                          scale, out, max_context_len, workspace, partition_tokens, k_scale, v_scale, stream)
 
 
 def merge(workspace, context_lens, out, max_context_len, partition_tokens=0, stream=None):

@@ -151,6 +151,11 @@ pa_status prepare_decode(const void* q, int32_t q_dtype, int32_t num_seqs, int32
   a.qk_scale = scale * kLog2e * ks;
   a.v_scale = is_scaled(cache->dtype) ? cache->v_scale : 1.0f;
   a.dense = num_seqs <= pa::kDenseMaxSeqs && (int64_t)ws.parts * a.head_groups * num_seqs < INT32_MAX;
+  a.k_new = nullptr;
+  a.v_new = nullptr;
+  a.k_cache_w = nullptr;
+  a.v_cache_w = nullptr;
+  a.inv_k = a.inv_v = 1.0f;
   call->kernel = k;
   call->ws = ws;
   return PA_OK;
@@ -332,6 +337,58 @@ pa_status pa_decode_partition(const void* q, int32_t q_dtype, int32_t num_seqs, 
                                      workspace_bytes, partition_tokens, kernel, &c);
   if (s != PA_OK) return s;
   return run_partition(c, stream);
+}
+
+// Decode with the step's token appended by the partition kernel itself.
+static pa_status prepare_append(const void* q, int32_t q_dtype, const void* k_new, const void* v_new, int32_t in_dtype,
+                                int32_t num_seqs, int32_t num_q_heads, void* k_cache, void* v_cache,
+                                const pa_kv_cache* cache, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                const int32_t* context_lens, int32_t max_context_len, float scale, void* out,
+                                void* workspace, size_t workspace_bytes, int32_t partition_tokens, DecodeCall* c) {
+  if (!k_new || !v_new) return PA_ERR_NULL;
+  const pa_status s = prepare_decode(q, q_dtype, num_seqs, num_q_heads, k_cache, v_cache, cache, block_tables,
+                                     max_blocks_per_seq, context_lens, max_context_len, scale, out, workspace,
+                                     workspace_bytes, partition_tokens, PA_KERNEL_MFMA, c);
+  if (s != PA_OK) return s;
+  if (in_dtype != PA_BF16) return PA_ERR_DTYPE;
+  if (c->args.partition_tokens < 256) return PA_ERR_UNSUPPORTED;
+  pa::DecodeArgs& a = c->args;
+  a.k_new = static_cast<const uint16_t*>(k_new);
+  a.v_new = static_cast<const uint16_t*>(v_new);
+  a.k_cache_w = static_cast<uint8_t*>(k_cache);
+  a.v_cache_w = static_cast<uint8_t*>(v_cache);
+  a.inv_k = is_scaled(cache->dtype) ? 1.0f / cache->k_scale : 1.0f;
+  a.inv_v = is_scaled(cache->dtype) ? 1.0f / cache->v_scale : 1.0f;
+  return PA_OK;
+}
+
+pa_status pa_decode_partition_append(const void* q, int32_t q_dtype, const void* k_new, const void* v_new,
+                                     int32_t in_dtype, int32_t num_seqs, int32_t num_q_heads, void* k_cache,
+                                     void* v_cache, const pa_kv_cache* cache, const int32_t* block_tables,
+                                     int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                     int32_t max_context_len, float scale, void* out, void* workspace,
+                                     size_t workspace_bytes, int32_t partition_tokens, void* stream) {
+  DecodeCall c;
+  const pa_status s = prepare_append(q, q_dtype, k_new, v_new, in_dtype, num_seqs, num_q_heads, k_cache, v_cache,
+                                     cache, block_tables, max_blocks_per_seq, context_lens, max_context_len, scale,
+                                     out, workspace, workspace_bytes, partition_tokens, &c);
+  if (s != PA_OK) return s;
+  return run_partition(c, stream);
+}
+
+pa_status pa_decode_append(const void* q, int32_t q_dtype, const void* k_new, const void* v_new, int32_t in_dtype,
+                           int32_t num_seqs, int32_t num_q_heads, void* k_cache, void* v_cache,
+                           const pa_kv_cache* cache, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                           const int32_t* context_lens, int32_t max_context_len, float scale, void* out,
+                           void* workspace, size_t workspace_bytes, int32_t partition_tokens, void* stream) {
+  DecodeCall c;
+  pa_status s = prepare_append(q, q_dtype, k_new, v_new, in_dtype, num_seqs, num_q_heads, k_cache, v_cache, cache,
+                               block_tables, max_blocks_per_seq, context_lens, max_context_len, scale, out,
+                               workspace, workspace_bytes, partition_tokens, &c);
+  if (s != PA_OK) return s;
+  s = run_partition(c, stream);
+  if (s != PA_OK) return s;
+  return run_merge(c, stream);
 }
 
 pa_status pa_decode(const void* q, int32_t q_dtype, int32_t num_seqs, int32_t num_q_heads, const void* k_cache,

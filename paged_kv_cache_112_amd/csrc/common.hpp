@@ -72,6 +72,14 @@ __device__ __forceinline__ uint32_t f32_to_e4m3(float y) {
   return sign | code;
 }
 
+// -- symmetric int8 -----------------------------------------------------------
+// Round to a symmetric int8 code: nearest, ties to even, saturating to +-127; NaN -> 0.
+__device__ __forceinline__ uint32_t f32_to_i8(float y) {
+  if (y != y) return 0u;
+  const float r = fminf(fmaxf(__builtin_rintf(y), -127.0f), 127.0f);
+  return (uint32_t)(int32_t)r & 0xffu;
+}
+
 // -- wave reductions ---------------------------------------------------------
 // DPP controls: quad_perm [1,0,3,2] (xor 1), quad_perm [2,3,0,1] (xor 2),
 // row_half_mirror (lane i <-> 7-i in each 8), row_mirror (i <-> 15-i in each 16).

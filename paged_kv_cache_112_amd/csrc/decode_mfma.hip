@@ -35,12 +35,19 @@
 // Tokens past the context are clamped to the last valid row for addressing (no
 // stray or out-of-range reads, never a table entry past the context) and given
 // probability 0.
+// The appending instantiation (pa_decode_append) also stores this step's token: the
+// workgroup whose partition holds position ctx - 1 writes the rows there first.
 #include "launch.hpp"
 #include "mfma_tiles.hpp"
 
 // K or V tiles in flight per wave (bf16 and e4m3 pools; 6 measured best for both).
 #ifndef PA_MFMA_DEPTH
 #define PA_MFMA_DEPTH 6
+#endif
+// The appending kernel (bf16 pools) keeps one tile less in flight: at 6 its register
+// demand spills.
+#ifndef PA_APPEND_DEPTH
+#define PA_APPEND_DEPTH 5
 #endif
 #ifndef PA_MFMA_DEPTH_FP8
 #define PA_MFMA_DEPTH_FP8 6
@@ -73,12 +80,42 @@ __device__ __forceinline__ int32_t load_uniform(const int32_t* p) {
   return *(const __attribute__((address_space(4))) int32_t*)p;
 }
 
+// The appended token's K and V rows of KV head kvh, written at position pos in the
+// pool's format: bf16 copied, e4m3 / int8 quantized exactly as pa_write_kv does (one
+// fp32 multiply by 1/scale, then the rounding).  Lanes 0 .. D/8 - 1 take 8-element
+// chunks of K, the next D/8 lanes those of V.
+template <int KF, int D>
+__device__ __forceinline__ void append_token(const DecodeArgs& a, int b, int kvh, int pos, int lane) {
+  constexpr int CH = D / 8;
+  constexpr int ESZ = byte_fmt(KF) ? 1 : 2;
+  if (lane >= 2 * CH) return;
+  const bool is_v = lane >= CH;
+  const int c = is_v ? lane - CH : lane;
+  const int32_t blk = a.block_tables[(int64_t)b * a.bt_stride + (pos >> a.log2_bs)];
+  const int64_t row = (int64_t)blk * a.block_size + (pos & (a.block_size - 1));
+  const u32x4 x = ld16((is_v ? a.v_new : a.k_new) + ((int64_t)b * a.num_kv_heads + kvh) * D + 8 * c);
+  uint8_t* dst = (is_v ? a.v_cache_w : a.k_cache_w) + row * a.row_bytes + (int64_t)(kvh * D + 8 * c) * ESZ;
+  if constexpr (!byte_fmt(KF)) {
+    st16(dst, x);
+  } else {
+    const float inv = is_v ? a.inv_v : a.inv_k;
+    u32x2 o = {0u, 0u};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float y = ((i & 1) ? bf16hi(x[i >> 1]) : bf16lo(x[i >> 1])) * inv;
+      const uint32_t code = KF == kFmtE4m3 ? f32_to_e4m3(y) : f32_to_i8(y);
+      o[i >> 2] |= code << (8 * (i & 3));
+    }
+    st8(dst, o);
+  }
+}
+
 // Query head g of the group sits in MFMA column n = 4 * (g % 4) + g / 4, so that
 // after P.V lane (n, q4) register r holds head 4 * r + q4: with G <= 4 every lane
 // of the wave holds one head's output in register 0.
 __device__ __forceinline__ int head_of_column(int n) { return 4 * (n & 3) + (n >> 2); }
 
-template <int KF, int D, int PT, bool BIGBS>
+template <int KF, int D, int PT, bool BIGBS, bool APPEND>
 __global__ __launch_bounds__(PA_WG_THREADS) __attribute__((amdgpu_waves_per_eu(PA_MIN_WAVES_PER_EU, PA_MAX_WAVES_PER_EU)))
 void decode_mfma_kernel(const DecodeArgs a) {
   // A partition of P = 16 * PT * W tokens is shared by W waves per KV head: wave w
@@ -89,7 +126,7 @@ void decode_mfma_kernel(const DecodeArgs a) {
   constexpr int ESZ = byte_fmt(KF) ? 1 : 2;
   constexpr int VEC = D / 16;
   constexpr int NKK = D / 32;
-  constexpr int DEPTH = byte_fmt(KF) ? PA_MFMA_DEPTH_FP8 : PA_MFMA_DEPTH;
+  constexpr int DEPTH = byte_fmt(KF) ? PA_MFMA_DEPTH_FP8 : (APPEND ? PA_APPEND_DEPTH : PA_MFMA_DEPTH);
   constexpr int KD = PT < DEPTH ? PT : DEPTH;
   __shared__ int32_t tbl[BIGBS ? 1 : kMaxPartitionTokens];
   extern __shared__ float xs[];     // combine area, W > 1 only
@@ -123,6 +160,18 @@ void decode_mfma_kernel(const DecodeArgs a) {
     uint16_t* o = out + ((int64_t)b * a.num_q_heads + hq0) * D;
     for (int i = lane; i < G * D / 8; i += kWave) st16(o + 8 * i, u32x4{0u, 0u, 0u, 0u});
     return;
+  }
+
+  // A token appended in this launch (position ctx - 1, at pa_write_kv's slot through
+  // the block table) is stored by the workgroup whose partition holds it before any of
+  // the partition's rows are read: the first wave of each KV head writes that head's
+  // rows, every store completes, and the workgroup meets at a barrier.
+  if constexpr (APPEND) {
+    if (ctx <= t0 + P) {
+      if (w == 0) append_token<KF, D>(a, b, kvh, ctx - 1, lane);
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+    }
   }
 
   const int lb0 = t0 >> a.log2_bs;
@@ -361,12 +410,18 @@ void decode_mfma_kernel(const DecodeArgs a) {
 template <int KF, int D, bool BIGBS>
 static hipError_t launch_pt(const DecodeArgs& a, dim3 grid, dim3 block, hipStream_t s) {
   const size_t lds = a.waves_per_head > 1 ? sizeof(float) * combine_floats(a.waves_per_head) * a.heads_per_wg : 0;
+  if (a.k_new != nullptr) {
+    // the appending kernel exists for 256-token tiles per wave (partitions of 256, 512, 1024)
+    if (a.partition_tokens / a.waves_per_head != 256) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((decode_mfma_kernel<KF, D, 16, BIGBS, true>), grid, block, lds, s, a);
+    return hipGetLastError();
+  }
   switch (a.partition_tokens / a.waves_per_head) {
-    case 16: hipLaunchKernelGGL((decode_mfma_kernel<KF, D, 1, BIGBS>), grid, block, lds, s, a); break;
-    case 32: hipLaunchKernelGGL((decode_mfma_kernel<KF, D, 2, BIGBS>), grid, block, lds, s, a); break;
-    case 64: hipLaunchKernelGGL((decode_mfma_kernel<KF, D, 4, BIGBS>), grid, block, lds, s, a); break;
-    case 128: hipLaunchKernelGGL((decode_mfma_kernel<KF, D, 8, BIGBS>), grid, block, lds, s, a); break;
-    case 256: hipLaunchKernelGGL((decode_mfma_kernel<KF, D, 16, BIGBS>), grid, block, lds, s, a); break;
+    case 16: hipLaunchKernelGGL((decode_mfma_kernel<KF, D, 1, BIGBS, false>), grid, block, lds, s, a); break;
+    case 32: hipLaunchKernelGGL((decode_mfma_kernel<KF, D, 2, BIGBS, false>), grid, block, lds, s, a); break;
+    case 64: hipLaunchKernelGGL((decode_mfma_kernel<KF, D, 4, BIGBS, false>), grid, block, lds, s, a); break;
+    case 128: hipLaunchKernelGGL((decode_mfma_kernel<KF, D, 8, BIGBS, false>), grid, block, lds, s, a); break;
+    case 256: hipLaunchKernelGGL((decode_mfma_kernel<KF, D, 16, BIGBS, false>), grid, block, lds, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

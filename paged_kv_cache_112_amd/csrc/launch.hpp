@@ -41,6 +41,13 @@ struct DecodeArgs {
   float v_scale;
   int32_t dense;             // 1: workgroup ids number only existing (sequence, partition) pairs
   int32_t waves_per_head;    // matrix-core path: waves sharing one KV head's partition (1, 2 or 4)
+  // Appended token (matrix-core grid kernel only; k_new == nullptr: none): bf16 rows
+  // [B, H_kv, D] written, in the pool's format, at position context_lens[b] - 1.
+  const uint16_t* k_new;
+  const uint16_t* v_new;
+  uint8_t* k_cache_w;        // the pools, writable (same addresses as k_cache, v_cache)
+  uint8_t* v_cache_w;
+  float inv_k, inv_v;        // fp32(1 / scale) for one-byte pools
 };
 
 // Partitions longer than 256 tokens are split among several waves of one workgroup

@@ -14,13 +14,6 @@ namespace pa {
 
 enum class WriteMode { kCopy16, kCopy32, kBf16ToE4m3, kF32ToE4m3, kBf16ToInt8, kF32ToInt8 };
 
-// Round to a symmetric int8 code: nearest, ties to even, saturating to +-127; NaN -> 0.
-__device__ __forceinline__ uint32_t f32_to_i8(float y) {
-  if (y != y) return 0u;
-  const float r = fminf(fmaxf(__builtin_rintf(y), -127.0f), 127.0f);
-  return (uint32_t)(int32_t)r & 0xffu;
-}
-
 template <WriteMode M>
 __global__ __launch_bounds__(256) void write_kv_kernel(const uint8_t* __restrict__ k, const uint8_t* __restrict__ v,
                                                        const int32_t* __restrict__ slots, uint8_t* __restrict__ kc,

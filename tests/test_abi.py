@@ -103,8 +103,34 @@ def test_decode_partition_and_merge_checks():
     assert pa.pa_merge(None, 0, 4, 4, 64, FAKE, 16, 16, pa.PA_F32, FAKE, None) == pa.PA_OK
 
 
+def _append(fn=None, **kw):
+    a = dict(q=FAKE, q_dtype=pa.PA_BF16, k_new=FAKE, v_new=FAKE, in_dtype=pa.PA_BF16, num_seqs=4, num_q_heads=4,
+             k_cache=FAKE, v_cache=FAKE, cache=_cache(dtype=pa.PA_BF16), block_tables=FAKE, max_blocks_per_seq=13,
+             context_lens=FAKE, max_context_len=200, scale=0.125, out=FAKE, workspace=FAKE, workspace_bytes=1 << 30,
+             partition_tokens=0, stream=None)
+    a.update(kw)
+    return (fn or pa.pa_decode_append)(**a)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(k_new=None), pa.PA_ERR_NULL),
+    (dict(v_new=None), pa.PA_ERR_NULL),
+    (dict(q=None), pa.PA_ERR_NULL),
+    (dict(in_dtype=pa.PA_F32), pa.PA_ERR_DTYPE),                        # rows come in bf16
+    (dict(cache=_cache(dtype=pa.PA_F32), q_dtype=pa.PA_F32), pa.PA_ERR_UNSUPPORTED),   # f32 pools: no matrix-core path
+    (dict(partition_tokens=128), pa.PA_ERR_UNSUPPORTED),                # the appending kernel takes 256-token tiles
+    (dict(partition_tokens=16), pa.PA_ERR_UNSUPPORTED),
+    (dict(num_q_heads=5), pa.PA_ERR_SHAPE),
+    (dict(workspace=None, max_blocks_per_seq=20, max_context_len=300), pa.PA_ERR_WORKSPACE),
+])
+def test_decode_append_rejects_bad_arguments(kw, status):
+    assert _append(**kw) == status
+    assert _append(pa.pa_decode_partition_append, **kw) == status
+
+
 def test_zero_sized_calls_enqueue_nothing():
     assert _decode(num_seqs=0) == pa.PA_OK
+    assert _append(num_seqs=0) == pa.PA_OK
     c = _cache(dtype=pa.PA_BF16)
     assert pa.pa_write_kv(FAKE, FAKE, pa.PA_BF16, 0, FAKE, FAKE, FAKE, c, None) == pa.PA_OK
 
