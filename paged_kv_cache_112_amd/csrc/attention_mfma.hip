@@ -10,7 +10,8 @@
 // block_tables, seq_lens and query_start_loc, the lower-triangular mask offset by
 // S - n, and the statement that the math equals contiguous attention).
 //
-// How, on gfx950: one wave per (request, KV head, run of NQ query groups).  A query
+// How, on gfx950: one wave per (request, KV head, run of NQ query groups), requests
+// taken longest first.  A query
 // group is T = 16 / G new tokens with all G query heads of the KV head: the 16
 // columns of one MFMA operand, (token, head) pairs, so the product is dense.  Each
 // K/V tile a wave loads (and, for one-byte pools, widens) serves all NQ groups.  The
@@ -57,6 +58,23 @@ __device__ __forceinline__ uint32_t pair_of(const uint32_t (&lo)[NW], const uint
   return (e & 1) ? pack_hi_halves(lo[e >> 1], hi[e >> 1]) : pack_lo_halves(lo[e >> 1], hi[e >> 1]);
 }
 
+// Requests are taken longest context first (ties by index), so the workgroups of the
+// longest run first and shorter ones fill the tail.  Up to 64 requests are ranked in
+// the kernel, one per lane; beyond that they are taken in index order.  Returns the
+// request of rank r (uniform).
+__device__ __forceinline__ int request_of_rank(const int32_t* seq_lens, int B, int r) {
+  if (B > kWave) return r;
+  const int lane = threadIdx.x & 63;
+  const int mine = lane < B ? seq_lens[lane] : 0;
+  int rank = 0;
+  for (int j = 0; j < B; ++j) {
+    const int other = __builtin_amdgcn_readlane(mine, j);
+    rank += (other > mine || (other == mine && j < lane)) ? 1 : 0;
+  }
+  const uint64_t hit = __builtin_amdgcn_ballot_w64(lane < B && rank == r);
+  return __builtin_amdgcn_readfirstlane((int)__builtin_ctzll(hit));
+}
+
 template <int KF, int D, bool BIGBS, int NQ>
 __global__ __launch_bounds__(256) void attention_mfma_kernel(const AttnArgs a) {
   constexpr int ESZ = byte_fmt(KF) ? 1 : 2;
@@ -64,7 +82,7 @@ __global__ __launch_bounds__(256) void attention_mfma_kernel(const AttnArgs a) {
   constexpr int NKK = D / 32;
   const int kvh = blockIdx.x % a.num_kv_heads;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int i = blockIdx.y;
+  const int i = request_of_rank(a.seq_lens, a.num_seqs, blockIdx.y);
   const int q0 = attn_load_uniform(a.query_start_loc + i);
   const int nq = attn_load_uniform(a.query_start_loc + i + 1) - q0;
   const int S = attn_load_uniform(a.seq_lens + i);
