@@ -332,10 +332,15 @@ def bench_graph_loop(args, torch, pa):
 
     def model_step():
         # one token for the whole model: the lengths advance once, every layer writes and decodes
+        # (--fused: the write done by the decode's partition launch)
         pa.slot_mapping(dbt, ctx, bs, slots, advance=True)
         for kc, vc in pools:
-            pa.write_kv(knew, vnew, slots, kc, vc)
-            pa.decode(q, kc, vc, dbt, ctx, w.scale, out=out, max_context_len=max_ctx, workspace=ws)
+            if args.fused:
+                pa.decode_append(q, knew, vnew, kc, vc, dbt, ctx, w.scale, out=out, max_context_len=max_ctx,
+                                 workspace=ws)
+            else:
+                pa.write_kv(knew, vnew, slots, kc, vc)
+                pa.decode(q, kc, vc, dbt, ctx, w.scale, out=out, max_context_len=max_ctx, workspace=ws)
 
     torch.cuda.synchronize()
     graph = torch.cuda.CUDAGraph()
@@ -354,7 +359,8 @@ def bench_graph_loop(args, torch, pa):
     torch.cuda.synchronize()
     us_layer = e0.elapsed_time(e1) * 1e3 / (reps * LAYERS)
     print(json.dumps({"metric": "device-side decode loop (slot mapping + write + decode per layer, graph replay)",
-                      "workload": WORKLOAD, "layers_per_graph": LAYERS, "model_steps": reps,
+                      "workload": WORKLOAD, "fused_write": bool(args.fused), "layers_per_graph": LAYERS,
+                      "model_steps": reps,
                       "us_per_layer_step": round(us_layer, 2),
                       "decode_tokens_per_s_per_layer": round(B / us_layer * 1e6, 1),
                       "note": "lengths grow by one token per replay; tables pre-filled for the growth"}))
