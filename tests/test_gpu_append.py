@@ -66,6 +66,17 @@ def test_append_against_oracle(kv):
     assert np.abs(got - ref).max() <= 2e-2
 
 
+def test_append_beyond_the_dense_grid():
+    """More than 1024 sequences: the partition grid is (partitions x heads, sequences), not the
+    dense numbering; fused and unfused still agree bit for bit."""
+    rng = np.random.default_rng(8)
+    ctx = rng.integers(1, 600, 1100)
+    w = custom_workload(ctx, 8, 2, 64, 16, seed=9)
+    _, a, b = _both(w, 256)
+    for x, y in zip(a, b):
+        assert np.array_equal(x.view(np.uint8), y.view(np.uint8))
+
+
 def test_append_llama3_8b_b64_full_size():
     """The batch-64 step at full size, fused against unfused, bit for bit."""
     w = make_config("llama3_8b_b64")
