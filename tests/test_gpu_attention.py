@@ -85,6 +85,17 @@ def test_mixed_query_lengths(hq, hkv, d, bs):
     assert np.abs(out_to_f64(m.run(scale)) - m.oracle(scale)).max() <= 2e-2
 
 
+@pytest.mark.parametrize("kv", ["e4m3", "i8"])
+@pytest.mark.parametrize("hq,hkv,d,bs", [(16, 8, 64, 16), (32, 2, 128, 4), (8, 8, 64, 64), (32, 4, 64, 1)])
+def test_one_byte_pools_across_shapes(kv, hq, hkv, d, bs):
+    """e4m3 and int8 pools over group sizes 2, 16, 1, 8, both head sizes and small / large blocks."""
+    seq_lens = [1, 40, 300, 17, 130]
+    qlens = [1, 40, 100, 16, 3]
+    m = MQ(seq_lens, qlens, hq, hkv, d, bs, kv, seed=hq + d + bs)
+    scale = float(np.float32(1 / np.sqrt(d)))
+    assert np.abs(out_to_f64(m.run(scale)) - m.oracle(scale)).max() <= 2e-2
+
+
 @pytest.mark.parametrize("kv", ["bf16", "e4m3", "i8"])
 def test_peaky_scores(kv):
     """A large scale makes each row nearly one-hot: a wrong key or mask shows as an O(1) error."""
