@@ -165,24 +165,42 @@ def bench_stream_read(args, torch):
     from workloads import make_config
     w = make_config(WORKLOAD)
     decode_bytes = algorithmic_bytes(w)["partition"] // 16 * 16
+    decode_bytes_1b = algorithmic_bytes(w, kv_bytes=1)["partition"] // 16 * 16     # one-byte pools
     buf = torch.ones((2 << 30) // 4, dtype=torch.int32, device=dev)
     grids = (512, 1024, 2048, 4096)
     out = torch.empty(max(grids) * 256, dtype=torch.int32, device=dev)
     stream = torch.cuda.current_stream().cuda_stream
     results = []
-    for nbytes in (decode_bytes, 2 << 30):
+    total = buf.numel() * 4
+    for nbytes in (decode_bytes, decode_bytes_1b, 2 << 30):
+        # successive launches read successive disjoint windows of the 2 GiB buffer, as the
+        # decode bench reads a different layer's pools each step, so the MALL cannot serve them
+        windows = total // nbytes
+        turn = [0]
+
+        def launch(grid):
+            off = (turn[0] % windows) * nbytes
+            turn[0] += 1
+            L.stream_read_launch(buf.data_ptr() + off, nbytes, out.data_ptr(), grid, stream)
+
         best = None
         for grid in grids:
-            us = _time_launches(torch, lambda: L.stream_read_launch(buf.data_ptr(), nbytes, out.data_ptr(), grid, stream),
-                                max(args.steps, 10), max(args.warmup, 3))
+            us = _time_launches(torch, lambda: launch(grid), max(args.steps, 10), max(args.warmup, 3))
             gbs = nbytes / us / 1e3
             if best is None or gbs > best[1]:
                 best = (grid, gbs, us)
-        results.append({"bytes": nbytes, "best_grid": best[0], "us": round(best[2], 2), "GB/s": round(best[1], 1),
+        results.append({"bytes": nbytes, "windows": windows, "best_grid": best[0], "us": round(best[2], 2),
+                        "GB/s": round(best[1], 1),
                         "frac_of_8TBps": round(best[1] / 8000.0, 4)})
+    # a plain device-to-device copy of 1 GiB (read + write), the reference for the copy-shaped operations
+    src = buf.view(torch.uint8)[: 1 << 30]
+    dst = torch.empty_like(src)
+    us = _time_launches(torch, lambda: dst.copy_(src), max(args.steps, 10), max(args.warmup, 3))
+    copy = {"bytes_read_and_written": 2 << 30, "us": round(us, 2), "GB/s": round((2 << 30) / us / 1e3, 1),
+            "frac_of_8TBps": round((2 << 30) / us / 1e3 / 8000.0, 4)}
     print(json.dumps({"metric": "plain streaming read (reference ceiling for the decode's HBM figure)",
-                      "results": results, "timing": "HIP events around back-to-back launches, best of grids " +
-                      str(list(grids))}))
+                      "results": results, "torch_copy_1GiB": copy,
+                      "timing": "HIP events around back-to-back launches, best of grids " + str(list(grids))}))
 
 
 def side_op(args, w, torch, pa):

