@@ -25,6 +25,9 @@
 #ifndef PA_PERSIST_DEPTH
 #define PA_PERSIST_DEPTH 4   // tiles in flight per wave; divides 2 * tiles per unit
 #endif
+#ifndef PA_PERSIST_DEPTH_BYTE
+#define PA_PERSIST_DEPTH_BYTE 8   // one-byte pools: tiles are half the bytes, so twice as many
+#endif
 
 namespace pa {
 
@@ -35,7 +38,8 @@ __global__ __launch_bounds__(256) void decode_persist_kernel(const DecodeArgs a)
   constexpr int VEC = D / 16;
   constexpr int NKK = D / 32;
   constexpr int NSTEP = 2 * PT;
-  constexpr int DEPTH = NSTEP < PA_PERSIST_DEPTH ? NSTEP : PA_PERSIST_DEPTH;
+  constexpr int RING = byte_fmt(KF) ? PA_PERSIST_DEPTH_BYTE : PA_PERSIST_DEPTH;
+  constexpr int DEPTH = NSTEP < RING ? NSTEP : RING;
   static_assert(NSTEP % DEPTH == 0, "ring depth must divide the steps of a unit");
   constexpr int NR = BIGBS ? 1 : (P + 63) / 64;   // block-table registers per lane
   using KT = KTile<KF, D>;

@@ -174,10 +174,11 @@ def test_bitwise_invariant_under_placement_and_block_size(kv, kernel):
         assert np.array_equal(o.view(np.uint8), outs[0].view(np.uint8))
 
 
-@pytest.mark.parametrize("P", [16, 64, 128])
-def test_persistent_and_grid_kernels_agree_bitwise(P):
+@pytest.mark.parametrize("kv", ["bf16", "e4m3", "i8"])
+@pytest.mark.parametrize("P", [16, 64, 128, 256])
+def test_persistent_and_grid_kernels_agree_bitwise(P, kv):
     """Both matrix-core schedules compute each partition in the same order: identical bits."""
-    w = custom_workload(EDGE_CTX + [1000, 2047], 32, 8, 128, 16, "bf16", "bf16", seed=41)
+    w = custom_workload(EDGE_CTX + [1000, 2047], 32, 8, 128, 16, kv, "bf16", seed=41)
     dev = DeviceInputs(build_host_inputs(w))
     a = from_dev(dev.decode(partition_tokens=P, kernel=2))
     b = from_dev(dev.decode(partition_tokens=P, kernel=3))
