@@ -204,6 +204,39 @@ def test_repeated_calls_on_one_workspace():
     assert np.abs(out_to_f64(res) - h.oracle_decode()).max() <= 2e-2
 
 
+_MANY = {}
+
+
+def _many_sequences(B, kv):
+    """B sequences of 0..299 tokens (zeros, 64/256-token boundaries and their neighbours sown
+    in), with their oracle output; cached, since it does not depend on the launch."""
+    if (B, kv) not in _MANY:
+        rng = np.random.default_rng(B)
+        ctx = rng.integers(0, 300, B)
+        ctx[::37] = 0
+        ctx[5::41] = 64
+        ctx[6::41] = 256
+        ctx[7::43] = 257
+        ctx[B - 1] = 299
+        w = custom_workload([int(c) for c in ctx], 8, 2, 64, 16, kv, "bf16", seed=53)
+        h = build_host_inputs(w)
+        _MANY[(B, kv)] = (w, h, h.oracle_decode())
+    return _MANY[(B, kv)]
+
+
+@pytest.mark.parametrize("kernel", [2, 3])
+@pytest.mark.parametrize("P", [64, 256])
+@pytest.mark.parametrize("B,kv", [(65, "bf16"), (777, "bf16"), (777, "e4m3"), (1024, "bf16")])
+def test_dense_numbering_over_many_sequence_chunks(B, kv, P, kernel):
+    """Between 65 and 1024 sequences both matrix-core schedules still number only existing
+    pairs, scanning the context lengths 64 at a time: every chunk boundary is crossed."""
+    w, h, ref = _many_sequences(B, kv)
+    print(f"decode {B} sequences kv={kv} P={P} kernel={kernel}", flush=True)
+    out = out_to_f64(DeviceInputs(h).decode(P, kernel))
+    assert np.isfinite(out).all()
+    assert np.abs(out - ref).max() <= TOL[kv]
+
+
 def test_large_batch_falls_back_to_grid_kernel():
     """More sequences than the persistent kernel's running total holds: the grid kernel runs instead."""
     ctx = [1 + (7 * i) % 90 for i in range(1100)]
