@@ -121,6 +121,19 @@ def test_scores_growing_along_the_context(kv):
     assert np.abs(out_to_f64(m.run(scale)) - m.oracle(scale)).max() <= 2e-2
 
 
+@pytest.mark.parametrize("B", [63, 64, 65, 130])
+def test_many_requests(B):
+    """Up to 64 requests are ranked longest first inside the kernel, beyond that taken in order:
+    both sides of the limit, with lengths that tie."""
+    rng = np.random.default_rng(B)
+    seq_lens = rng.integers(1, 200, B)
+    seq_lens[::9] = 96                                # ties
+    qlens = np.minimum(seq_lens, rng.integers(0, 40, B))
+    m = MQ(seq_lens, qlens, 16, 4, 64, 16, seed=B)
+    scale = 0.125
+    assert np.abs(out_to_f64(m.run(scale)) - m.oracle(scale)).max() <= 2e-2
+
+
 def test_one_token_per_sequence_matches_decode():
     import torch
     import paged_kv_cache_112_amd as pa
