@@ -76,6 +76,16 @@ def test_block_sizes(bs, kv, kernel):
     _check(DeviceInputs(build_host_inputs(w)), w, partition_tokens=64, kernel=KERNELS[kernel])
 
 
+@pytest.mark.parametrize("bs", [512, 1024])
+@pytest.mark.parametrize("kv,kernel,P", [("bf16", "mfma", 64), ("bf16", "mfma", 256), ("bf16", "mfma", 1024),
+                                         ("f32", "valu", 128), ("e4m3", "mfma", 256), ("i8", "persist", 64)])
+def test_largest_block_sizes(bs, kv, kernel, P):
+    """Blocks of 512 and 1024 tokens (the largest accepted), contexts crossing several of them."""
+    w = custom_workload([2100, 1, 1024, 1025, 513, 0, 3000], 8, 2, 128, bs, kv, "f32" if kv == "f32" else "bf16",
+                        seed=bs + P)
+    _check(DeviceInputs(build_host_inputs(w)), w, partition_tokens=P, kernel=KERNELS[kernel])
+
+
 # partitions of 512 and 1024 tokens: 2 or 4 waves per KV head, combined on chip
 LONG_EDGE_CTX = EDGE_CTX + [767, 768, 769, 1023, 1024, 1025, 2047, 2048, 2049, 3000]
 
