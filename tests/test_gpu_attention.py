@@ -76,7 +76,7 @@ def test_printed_check(kv):
 
 
 @pytest.mark.parametrize("hq,hkv,d", [(8, 8, 128), (16, 8, 64), (32, 8, 128), (32, 4, 64), (32, 2, 128)])
-@pytest.mark.parametrize("bs", [1, 4, 16, 64])
+@pytest.mark.parametrize("bs", [1, 4, 16, 64, 1024])
 def test_mixed_query_lengths(hq, hkv, d, bs):
     seq_lens = [1, 5, 40, 300, 17, 130, 64]
     qlens = [1, 5, 3, 300, 16, 17, 1]

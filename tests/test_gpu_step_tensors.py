@@ -13,7 +13,7 @@ pytestmark = pytest.mark.gpu
 
 @pytest.mark.parametrize("multi", [False, True])
 @pytest.mark.parametrize("advance", [False, True])
-@pytest.mark.parametrize("bs", [1, 4, 16, 256])
+@pytest.mark.parametrize("bs", [1, 4, 16, 256, 1024])
 def test_slot_mapping_matches_oracle(multi, advance, bs):
     import torch
     import paged_kv_cache_112_amd as pa
