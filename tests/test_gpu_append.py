@@ -34,7 +34,7 @@ def _both(w, P, hq_scale=None):
 
 
 @pytest.mark.parametrize("kv", ["bf16", "e4m3", "i8"])
-@pytest.mark.parametrize("bs", [1, 16, 64])
+@pytest.mark.parametrize("bs", [1, 16, 64, 1024])
 @pytest.mark.parametrize("P", [256, 512, 1024])
 def test_append_equals_write_then_decode(kv, bs, P):
     w = custom_workload(EDGES, 32, 8, 128, bs, kv=kv, seed=bs + P)
