@@ -28,8 +28,11 @@
  *     anything is enqueued and leaves all outputs untouched.  A failed launch
  *     returns PA_ERR_HIP.
  *   - Invalid *data* is undefined behaviour: a slot or block id outside the
- *     pool, context_lens[b] > max_blocks_per_seq * block_size, duplicate slots
- *     in one write, or an `out` that aliases an input.
+ *     pool, context_lens[b] > max_blocks_per_seq * block_size, context_lens[b] >
+ *     max_context_len (the decode then covers only the first
+ *     ceil(max_context_len / P) partitions of that sequence, and never writes
+ *     outside the workspace), duplicate slots in one write, or an `out` that
+ *     aliases an input.
  *
  * Pool layout (both pools, same shape and format):
  *   [num_blocks, block_size, num_kv_heads, head_dim]
@@ -158,11 +161,8 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t 
 typedef enum pa_kernel {
   PA_KERNEL_AUTO = 0,      /* matrix-core path for bf16/e4m3/int8 pools, vector path for f32 */
   PA_KERNEL_VALU = 1,      /* vector-ALU path (all formats, query-head group <= 8) */
-  PA_KERNEL_MFMA = 2,      /* matrix-core path, one workgroup per (sequence, partition, up to
+  PA_KERNEL_MFMA = 2       /* matrix-core path, one workgroup per (sequence, partition, up to
                               four KV heads) (bf16 q with bf16, e4m3 or int8 pools, group <= 16) */
-  PA_KERNEL_MFMA_PERSIST = 3 /* matrix-core path, persistent workgroups that each stream a
-                              contiguous range of work units (same inputs; num_seqs > 1024
-                              runs PA_KERNEL_MFMA instead) */
 } pa_kernel;
 
 /* Paged decode attention for one new token per sequence.
@@ -198,6 +198,8 @@ typedef enum pa_kernel {
  * Outputs are bf16-rounded (nearest even) for bf16 q.  The matrix-core path
  * rounds the softmax probabilities to bf16 before P.V (and sums the same
  * rounded values in the denominator).
+ * Launches: the partition stage (pa_decode_partition), then, when J > 1, the merge
+ * (pa_merge); the output is bit for bit that of those two calls.
  * Errors: PA_ERR_NULL, PA_ERR_SHAPE, PA_ERR_DTYPE, PA_ERR_UNSUPPORTED,
  * PA_ERR_WORKSPACE, PA_ERR_HIP.  num_seqs == 0 is a no-op returning PA_OK. */
 pa_status pa_decode(const void* q, int32_t q_dtype, int32_t num_seqs, int32_t num_q_heads,
@@ -321,6 +323,31 @@ pa_status pa_paged_attention(const void* q, int32_t q_dtype, int32_t num_tokens,
 pa_status pa_slot_mapping(const int32_t* block_tables, int32_t max_blocks_per_seq, int32_t* seq_lens,
                           const int32_t* query_start_loc, int32_t num_seqs, int32_t num_tokens, int32_t block_size,
                           int32_t advance, int32_t* slot_mapping, void* stream);
+
+/* Host-side contract checks.  Unlike every other call these take HOST pointers: the
+ * integer inputs of a step, inspected on the CPU before they go to the GPU.  The release
+ * kernels trust these contracts (a broken one is undefined behaviour, see above); a
+ * checked caller runs these first and refuses the step.  Each returns PA_OK, or
+ * PA_ERR_SHAPE with *bad_index (if not NULL) naming the first offending entry, or
+ * PA_ERR_NULL / PA_ERR_SHAPE for bad sizes (then *bad_index = -1).
+ *
+ * pa_check_decode_inputs: every context_lens[b] must lie in [0, max_context_len] and fit
+ * its table (<= max_blocks_per_seq * block_size) -- *bad_index = b otherwise; every table
+ * entry a decode reads (index j < ceil(context_lens[b] / block_size) of row b) must be a
+ * block of the pool, [0, num_blocks) -- *bad_index = b * max_blocks_per_seq + j otherwise.
+ * Entries past a sequence's context are padding and are not checked (LLM stack book, "From
+ * Python bookkeeping to the tensors the kernel actually takes": rows are padded to the
+ * longest sequence).
+ *
+ * pa_check_slots: every slot_mapping[i] >= 0 must be < num_blocks * block_size, and no two
+ * tokens may share a slot (the write would race); *bad_index = i of the out-of-range token,
+ * or of the first token, in token order, whose slot an earlier token already took.
+ * Negative slots are padding and pass. */
+pa_status pa_check_decode_inputs(const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                 const int32_t* context_lens, int32_t num_seqs, int32_t max_context_len,
+                                 int64_t num_blocks, int32_t block_size, int64_t* bad_index);
+pa_status pa_check_slots(const int32_t* slot_mapping, int32_t num_tokens, int64_t num_blocks, int32_t block_size,
+                         int64_t* bad_index);
 
 /* Static, human-readable name of a status code. */
 const char* pa_status_str(pa_status status);

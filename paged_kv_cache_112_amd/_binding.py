@@ -11,18 +11,21 @@ import ctypes
 import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libpa.so")
+# the in-tree build; PA_LIB names another build of the same sources (e.g. one made with
+# extra compile flags by build.build(out_path=...))
+LIB_PATH = os.environ.get("PA_LIB") or os.path.join(HERE, "libpa.so")
 
 # pa_status
 PA_OK, PA_ERR_NULL, PA_ERR_SHAPE, PA_ERR_DTYPE, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_HIP = range(7)
 # pa_dtype
 PA_F32, PA_BF16, PA_FP8_E4M3, PA_INT8 = 0, 1, 2, 3
 # pa_kernel
-PA_KERNEL_AUTO, PA_KERNEL_VALU, PA_KERNEL_MFMA, PA_KERNEL_MFMA_PERSIST = 0, 1, 2, 3
+PA_KERNEL_AUTO, PA_KERNEL_VALU, PA_KERNEL_MFMA = 0, 1, 2
 
 EXPORTED = ("pa_write_kv", "pa_copy_blocks", "pa_copy_blocks_layers", "pa_paged_attention", "pa_slot_mapping", "pa_decode", "pa_decode_partition", "pa_merge",
             "pa_decode_append", "pa_decode_partition_append",
-            "pa_decode_workspace_bytes", "pa_default_partition_tokens", "pa_status_str")
+            "pa_decode_workspace_bytes", "pa_default_partition_tokens", "pa_status_str",
+            "pa_check_decode_inputs", "pa_check_slots")
 
 
 class PaKvCache(ctypes.Structure):
@@ -79,6 +82,10 @@ def lib() -> ctypes.CDLL:
         L.pa_decode_workspace_bytes.restype = _sz
         L.pa_default_partition_tokens.argtypes = []
         L.pa_default_partition_tokens.restype = _i32
+        L.pa_check_decode_inputs.argtypes = [_vp, _i32, _vp, _i32, _i32, _i64, _i32, ctypes.POINTER(_i64)]
+        L.pa_check_decode_inputs.restype = ctypes.c_int
+        L.pa_check_slots.argtypes = [_vp, _i32, _i64, _i32, ctypes.POINTER(_i64)]
+        L.pa_check_slots.restype = ctypes.c_int
         L.pa_status_str.argtypes = [ctypes.c_int]
         L.pa_status_str.restype = ctypes.c_char_p
         _lib = L
@@ -169,6 +176,46 @@ def pa_decode_workspace_bytes(num_seqs, num_q_heads, head_dim, max_context_len, 
 
 def pa_default_partition_tokens() -> int:
     return lib().pa_default_partition_tokens()
+
+
+def _host_i32(a):
+    """A contiguous host int32 numpy array of a numpy array, list or (device) torch tensor."""
+    import numpy as np
+    if hasattr(a, "detach"):
+        a = a.detach().cpu().numpy()
+    a = np.ascontiguousarray(a, dtype=np.int32)
+    return a
+
+
+def check_decode_inputs(block_tables, context_lens, num_blocks, block_size, max_context_len=None):
+    """pa_check_decode_inputs on host copies: None when the decode's integer inputs keep the
+    contract, else the flat index of the first offending entry (see include/pa.h)."""
+    bt, ctx = _host_i32(block_tables), _host_i32(context_lens)
+    if bt.ndim != 2 or ctx.ndim != 1 or bt.shape[0] != ctx.shape[0]:
+        raise ValueError("block_tables [B, max_blocks] and context_lens [B] expected")
+    if max_context_len is None:
+        max_context_len = bt.shape[1] * block_size
+    bad = _i64(-1)
+    st = lib().pa_check_decode_inputs(bt.ctypes.data, bt.shape[1], ctx.ctypes.data, ctx.shape[0],
+                                      int(max_context_len), int(num_blocks), int(block_size), ctypes.byref(bad))
+    if st == PA_OK:
+        return None
+    if bad.value < 0:
+        check(st)
+    return bad.value
+
+
+def check_slots(slot_mapping, num_blocks, block_size):
+    """pa_check_slots on a host copy: None when every slot is in the pool and none repeats,
+    else the index of the first offending token (see include/pa.h)."""
+    sl = _host_i32(slot_mapping).reshape(-1)
+    bad = _i64(-1)
+    st = lib().pa_check_slots(sl.ctypes.data, sl.shape[0], int(num_blocks), int(block_size), ctypes.byref(bad))
+    if st == PA_OK:
+        return None
+    if bad.value < 0:
+        check(st)
+    return bad.value
 
 
 # ---------------------------------------------------------------------------

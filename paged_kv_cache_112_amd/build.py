@@ -17,17 +17,13 @@ LIB_NAME = "libpa.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
 ARCH = "gfx950"
 
-SOURCES = ["api.cpp", "write_kv.hip", "copy_blocks.hip", "attention_mfma.hip", "step_tensors.hip", "decode_mfma.hip", "decode_persist.hip", "decode_valu.hip", "merge.hip"]
+SOURCES = ["api.cpp", "check.cpp", "write_kv.hip", "copy_blocks.hip", "attention_mfma.hip", "step_tensors.hip", "decode_mfma.hip", "decode_valu.hip", "merge.hip"]
 
-# Packed-fp32 instructions are disabled on purpose; fp32 denormals are kept.  The
-# atomic optimizer is off: it turns the one-lane work-counter atomic of the persistent
-# decode kernel into a wave-aggregated one whose result is read at once, which makes
-# the wave wait for every load it has in flight.
+# Packed-fp32 instructions are disabled on purpose; fp32 denormals are kept.
 COMMON_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-fno-gpu-flush-denormals-to-zero",
-    "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
     "-Wall", "-Wno-unused-function", "-Wno-unused-command-line-argument",
     "-I" + os.path.join(ROOT, "include"),
 ]

@@ -101,11 +101,10 @@ pa_status prepare_decode(const void* q, int32_t q_dtype, int32_t num_seqs, int32
   const int32_t group = num_q_heads / cache->num_kv_heads;
   const int32_t P = partition_tokens == 0 ? kDefaultPartition : partition_tokens;
   if (!valid_partition(P)) return PA_ERR_UNSUPPORTED;
-  if (kernel < PA_KERNEL_AUTO || kernel > PA_KERNEL_MFMA_PERSIST) return PA_ERR_UNSUPPORTED;
+  if (kernel < PA_KERNEL_AUTO || kernel > PA_KERNEL_MFMA) return PA_ERR_UNSUPPORTED;
   int32_t k = kernel;
   if (k == PA_KERNEL_AUTO) k = f32_pair ? PA_KERNEL_VALU : PA_KERNEL_MFMA;
-  if (k == PA_KERNEL_MFMA_PERSIST && num_seqs > pa::kPersistMaxSeqs) k = PA_KERNEL_MFMA;
-  if ((k == PA_KERNEL_MFMA || k == PA_KERNEL_MFMA_PERSIST) && (f32_pair || group > 16)) return PA_ERR_UNSUPPORTED;
+  if (k == PA_KERNEL_MFMA && (f32_pair || group > 16)) return PA_ERR_UNSUPPORTED;
   if (k == PA_KERNEL_VALU && group > 8) return PA_ERR_UNSUPPORTED;
   // partitions beyond 256 tokens: matrix-core grid kernel only (several waves per KV head)
   if (P > 256 && k != PA_KERNEL_MFMA) return PA_ERR_UNSUPPORTED;
@@ -164,11 +163,10 @@ pa_status prepare_decode(const void* q, int32_t q_dtype, int32_t num_seqs, int32
 pa_status run_partition(const DecodeCall& c, void* stream) {
   if (c.args.num_seqs == 0) return PA_OK;
   const hipStream_t s = static_cast<hipStream_t>(stream);
-  const hipError_t e = c.kernel == PA_KERNEL_MFMA_PERSIST ? pa::launch_decode_persist(c.args, s)
-                       : c.kernel == PA_KERNEL_MFMA         ? pa::launch_decode_mfma(c.args, s)
-                                                            : pa::launch_decode_valu(c.args, s);
+  const hipError_t e = c.kernel == PA_KERNEL_MFMA ? pa::launch_decode_mfma(c.args, s) : pa::launch_decode_valu(c.args, s);
   return e == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
+
 
 pa_status run_merge(const DecodeCall& c, void* stream) {
   if (c.args.num_seqs == 0 || c.ws.parts <= 1) return PA_OK;

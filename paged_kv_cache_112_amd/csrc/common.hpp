@@ -124,7 +124,9 @@ __device__ __forceinline__ float wave_sum(float x) { return group_sum<64>(x); }
 // first: every full partition (sequence by sequence), then every shorter one, so the
 // last workgroups handed out are the short ones.  Every lane of the wave gets pair
 // x's sequence, partition and context length; returns false when x is past the last
-// pair.  All context lengths are loaded at once (up to kDenseMaxSeqs sequences).
+// pair.  A sequence contributes at most max_parts pairs (the grid holds max_parts per
+// sequence), so a context beyond the launch's max_context_len only loses its own later
+// partitions.  All context lengths are loaded at once (up to kDenseMaxSeqs sequences).
 constexpr int kDenseMaxSeqs = 1024;
 
 // Inclusive prefix sum over the wave, on DPP: shifts right by 1, 2, 4 and 8 lanes
@@ -145,8 +147,8 @@ __device__ __forceinline__ int wave_scan(int v) {
   return v;
 }
 
-__device__ __forceinline__ bool locate_partition(const int32_t* __restrict__ context_lens, int B, int P, int x,
-                                                 int& b_out, int& part_out, int& ctx_out) {
+__device__ __forceinline__ bool locate_partition(const int32_t* __restrict__ context_lens, int B, int P,
+                                                 int max_parts, int x, int& b_out, int& part_out, int& ctx_out) {
   constexpr int NC = kDenseMaxSeqs / 64;
   const int lane = threadIdx.x & 63;
   const int log2p = __builtin_ctz((unsigned)P);   // P is a power of two
@@ -165,7 +167,11 @@ __device__ __forceinline__ bool locate_partition(const int32_t* __restrict__ con
     for (int k = 0; k < NC; ++k) {
       if (64 * k >= B) break;
       const int c = cx[k];
-      const int n = c < 0 ? 0 : pass == 0 ? c >> log2p : ((c & (P - 1)) != 0 || c == 0 ? 1 : 0);
+      // at most max_parts partitions per sequence: a context beyond the launch's bound
+      // (a broken caller contract) loses its later partitions, never another sequence's
+      const int n = c < 0 ? 0
+                    : pass == 0 ? min(c >> log2p, max_parts)
+                                : (((c & (P - 1)) != 0 || c == 0) && (c >> log2p) < max_parts ? 1 : 0);
       const int incl = wave_scan(n) + base;
       const int tot = __builtin_amdgcn_readlane(incl, 63);
       if (x < tot) {

@@ -75,7 +75,7 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(const DecodeArgs a) {
   if (a.dense) {
     // workgroup x / head_groups is the x-th existing (sequence, partition) pair;
     // the grid's surplus workgroups come last and leave at once
-    if (!locate_partition(a.context_lens, a.num_seqs, P, blockIdx.x / a.head_groups, b, part, ctx)) return;
+    if (!locate_partition(a.context_lens, a.num_seqs, P, a.max_parts, blockIdx.x / a.head_groups, b, part, ctx)) return;
   } else {
     b = blockIdx.y;
     part = blockIdx.x / a.head_groups;

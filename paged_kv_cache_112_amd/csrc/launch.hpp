@@ -50,15 +50,20 @@ struct DecodeArgs {
   float inv_k, inv_v;        // fp32(1 / scale) for one-byte pools
 };
 
+// Launches with at most this many partitions per sequence merge with one 16-lane row per
+// query head (merge_rows.hpp); longer ones use the merge kernel's partition-parallel
+// schedule.
+#ifndef PA_ROW_MERGE_MAX_PARTS
+#define PA_ROW_MERGE_MAX_PARTS 16
+#endif
+constexpr int kRowMergeMaxParts = PA_ROW_MERGE_MAX_PARTS;
+
 // Partitions longer than 256 tokens are split among several waves of one workgroup
 // (matrix-core path), whose pieces are combined through LDS.
 constexpr int kMaxPartitionTokens = 1024;
 constexpr int kMaxWavesPerHead = 4;
 constexpr int kCombineO = 4 * 64 * 8;   // floats of one wave's O registers (4 rows r, 64 lanes, up to 8 columns)
 __host__ __device__ constexpr int combine_floats(int waves) { return 32 * waves + (waves - 1) * kCombineO; }
-
-// Largest batch the persistent kernel takes (its per-workgroup running total lives in LDS).
-constexpr int kPersistMaxSeqs = 1024;
 
 // Row of the workspace pieces of (sequence b, partition j, query head h): the
 // pieces are laid out partition-major, m / l [B, J, H] and o [B, J, H, D], so the
@@ -119,7 +124,6 @@ hipError_t launch_attention_mfma(const AttnArgs& a, hipStream_t stream);
 int attention_tokens_per_workgroup(int log2_group);
 hipError_t launch_copy_blocks(const CopyArgs& a, hipStream_t stream);
 hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t stream);
-hipError_t launch_decode_persist(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_decode_valu(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t stream);
 

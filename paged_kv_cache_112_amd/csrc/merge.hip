@@ -7,11 +7,18 @@
 // over the sequence dimension and the pieces reduced afterwards; the rescaling
 // is the running-max correction of its online softmax).  Sequences that fit in
 // one partition were finished by the partition kernel and are skipped here.
-// One wave per (query head, sequence): four groups of 16 lanes each take every
-// fourth partition, each lane owning head_dim / 16 columns; the groups are summed
-// with cross-lane adds at the end.
+//
+// Two schedules, chosen by the launch's partition count J (max_parts):
+//   * J <= kRowMergeMaxParts: merge_rows_kernel, one wave per (sequence, four query
+//     heads), one 16-lane row per head (merge_rows.hpp).
+//   * longer: merge_kernel, one wave per (query head, sequence): four groups of 16
+//     lanes each take every fourth partition, each lane owning head_dim / 16
+//     columns; the groups are summed with cross-lane adds at the end.
+// A sequence longer than the launch's J partitions (a context beyond
+// max_context_len, which the caller must not pass) is merged over its first J.
 #include "common.hpp"
 #include "launch.hpp"
+#include "merge_rows.hpp"
 
 namespace pa {
 
@@ -25,7 +32,7 @@ __global__ __launch_bounds__(64) void merge_kernel(const MergeArgs a) {
   const int pg = lane >> 4;
   const int d0 = (lane & 15) * DPL;
   const int ctx = a.context_lens[b];
-  const int n = (ctx + a.partition_tokens - 1) / a.partition_tokens;
+  const int n = min((ctx + a.partition_tokens - 1) / a.partition_tokens, a.max_parts);
   if (n <= 1) return;
   // pieces are partition-major: partition j of this (sequence, head) is row piece_row(b, j, h)
   const int64_t r0 = piece_row(b, 0, h, a.max_parts, a.num_q_heads);
@@ -103,10 +110,32 @@ __global__ __launch_bounds__(64) void merge_kernel(const MergeArgs a) {
   }
 }
 
+template <int D, int OF>
+__global__ __launch_bounds__(64) void merge_rows_kernel(const MergeArgs a) {
+  const int b = blockIdx.y;
+  const int lane = threadIdx.x;
+  const int h = 4 * blockIdx.x + (lane >> 4);
+  const int ctx = a.context_lens[b];
+  const int n = min((ctx + a.partition_tokens - 1) / a.partition_tokens, a.max_parts);
+  if (n <= 1 || h >= a.num_q_heads) return;     // uniform per 16-lane row
+  merge_head_row<D, OF>(a.ws_m, a.ws_l, a.ws_o, a.max_parts, a.num_q_heads, b, h, n, lane & 15, a.out);
+}
+
 hipError_t launch_merge(const MergeArgs& a, hipStream_t s) {
   if (a.max_parts <= 1 || a.num_seqs == 0) return hipSuccess;
-  const dim3 grid((unsigned)a.num_q_heads, (unsigned)a.num_seqs);
   const dim3 block(kWave);
+  if (a.max_parts <= kRowMergeMaxParts) {
+    const dim3 grid((unsigned)((a.num_q_heads + 3) / 4), (unsigned)a.num_seqs);
+    if (a.head_dim == 128) {
+      if (a.out_fmt == kF32) hipLaunchKernelGGL((merge_rows_kernel<128, kF32>), grid, block, 0, s, a);
+      else hipLaunchKernelGGL((merge_rows_kernel<128, kBf16>), grid, block, 0, s, a);
+    } else {
+      if (a.out_fmt == kF32) hipLaunchKernelGGL((merge_rows_kernel<64, kF32>), grid, block, 0, s, a);
+      else hipLaunchKernelGGL((merge_rows_kernel<64, kBf16>), grid, block, 0, s, a);
+    }
+    return hipGetLastError();
+  }
+  const dim3 grid((unsigned)a.num_q_heads, (unsigned)a.num_seqs);
   if (a.head_dim == 128) {
     if (a.out_fmt == kF32) hipLaunchKernelGGL((merge_kernel<128, kF32>), grid, block, 0, s, a);
     else hipLaunchKernelGGL((merge_kernel<128, kBf16>), grid, block, 0, s, a);

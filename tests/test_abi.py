@@ -82,7 +82,7 @@ def _decode(**kw):
     (dict(partition_tokens=512), pa.PA_ERR_UNSUPPORTED),                 # f32: vector path, <= 256 only
     (dict(kernel=pa.PA_KERNEL_MFMA), pa.PA_ERR_UNSUPPORTED),            # f32 has no matrix-core path
     (dict(kernel=9), pa.PA_ERR_UNSUPPORTED),
-    (dict(kernel=pa.PA_KERNEL_MFMA_PERSIST), pa.PA_ERR_UNSUPPORTED),
+    (dict(kernel=3), pa.PA_ERR_UNSUPPORTED),                            # no third schedule
     (dict(num_q_heads=32, cache=_cache(num_kv_heads=2), kernel=pa.PA_KERNEL_VALU), pa.PA_ERR_UNSUPPORTED),
     (dict(workspace=None, partition_tokens=16), pa.PA_ERR_WORKSPACE),
     (dict(workspace_bytes=100, partition_tokens=16), pa.PA_ERR_WORKSPACE),

@@ -13,7 +13,7 @@ from workloads import make_config
 pytestmark = pytest.mark.gpu
 
 TOL = {"f32": 1e-5, "bf16": 2e-2, "e4m3": 2e-2, "i8": 2e-2}
-KERNELS = {"valu": 1, "mfma": 2, "persist": 3}
+KERNELS = {"valu": 1, "mfma": 2}
 
 
 def _check(dev, w, partition_tokens=0, kernel=0, tol=None, scale=None):
@@ -58,9 +58,8 @@ EDGE_CTX = [1, 2, 15, 16, 17, 31, 255, 256, 257, 300, 511, 513, 0, 64]
 
 
 @pytest.mark.parametrize("kv,q,kernel", [("f32", "f32", "valu"), ("bf16", "bf16", "mfma"), ("bf16", "bf16", "valu"),
-                                         ("bf16", "bf16", "persist"), ("e4m3", "bf16", "mfma"), ("e4m3", "bf16", "valu"),
-                                         ("e4m3", "bf16", "persist"), ("i8", "bf16", "mfma"), ("i8", "bf16", "valu"),
-                                         ("i8", "bf16", "persist")])
+                                         ("e4m3", "bf16", "mfma"), ("e4m3", "bf16", "valu"), ("i8", "bf16", "mfma"),
+                                         ("i8", "bf16", "valu")])
 @pytest.mark.parametrize("hq,hkv,d", [(32, 8, 128), (8, 8, 64), (16, 2, 128)])
 @pytest.mark.parametrize("P", [0, 64])
 def test_edge_lengths(kv, q, kernel, hq, hkv, d, P):
@@ -69,8 +68,7 @@ def test_edge_lengths(kv, q, kernel, hq, hkv, d, P):
 
 
 @pytest.mark.parametrize("bs", [1, 2, 8, 64, 256])
-@pytest.mark.parametrize("kv,kernel", [("bf16", "mfma"), ("f32", "valu"), ("e4m3", "mfma"), ("bf16", "persist"),
-                                       ("i8", "mfma")])
+@pytest.mark.parametrize("kv,kernel", [("bf16", "mfma"), ("f32", "valu"), ("e4m3", "mfma"), ("i8", "mfma")])
 def test_block_sizes(bs, kv, kernel):
     w = custom_workload([300, 1, 47, 129], 8, 2, 128, bs, kv, "f32" if kv == "f32" else "bf16", seed=bs)
     _check(DeviceInputs(build_host_inputs(w)), w, partition_tokens=64, kernel=KERNELS[kernel])
@@ -78,7 +76,7 @@ def test_block_sizes(bs, kv, kernel):
 
 @pytest.mark.parametrize("bs", [512, 1024])
 @pytest.mark.parametrize("kv,kernel,P", [("bf16", "mfma", 64), ("bf16", "mfma", 256), ("bf16", "mfma", 1024),
-                                         ("f32", "valu", 128), ("e4m3", "mfma", 256), ("i8", "persist", 64)])
+                                         ("f32", "valu", 128), ("e4m3", "mfma", 256), ("i8", "mfma", 64)])
 def test_largest_block_sizes(bs, kv, kernel, P):
     """Blocks of 512 and 1024 tokens (the largest accepted), contexts crossing several of them."""
     w = custom_workload([2100, 1, 1024, 1025, 513, 0, 3000], 8, 2, 128, bs, kv, "f32" if kv == "f32" else "bf16",
@@ -173,45 +171,128 @@ def test_peaky_softmax(kv, kernel):
 # ---------------------------------------------------------------------------
 # invariances (bitwise on the GPU: reduction order depends on logical positions only)
 # ---------------------------------------------------------------------------
-@pytest.mark.parametrize("kv,kernel", [("bf16", 2), ("f32", 1), ("e4m3", 2), ("bf16", 3)])
-def test_bitwise_invariant_under_placement_and_block_size(kv, kernel):
+@pytest.mark.parametrize("kv,kernel", [("bf16", 2), ("f32", 1), ("e4m3", 2)])
+@pytest.mark.parametrize("P", [128, 256])
+def test_bitwise_invariant_under_placement_and_block_size(kv, kernel, P):
     q = "f32" if kv == "f32" else "bf16"
     outs = []
     for bs, perm_seed in [(16, 1), (16, 2), (1, 3), (64, 4), (256, 5)]:
         w = custom_workload([35, 300, 1, 520], 8, 2, 128, bs, kv, q, seed=21, perm_seed=perm_seed)
-        outs.append(from_dev(DeviceInputs(build_host_inputs(w)).decode(partition_tokens=128, kernel=kernel)))
+        outs.append(from_dev(DeviceInputs(build_host_inputs(w)).decode(partition_tokens=P, kernel=kernel)))
     for o in outs[1:]:
         assert np.array_equal(o.view(np.uint8), outs[0].view(np.uint8))
 
 
-@pytest.mark.parametrize("kv", ["bf16", "e4m3", "i8"])
-@pytest.mark.parametrize("P", [16, 64, 128, 256])
-def test_persistent_and_grid_kernels_agree_bitwise(P, kv):
-    """Both matrix-core schedules compute each partition in the same order: identical bits."""
-    w = custom_workload(EDGE_CTX + [1000, 2047], 32, 8, 128, 16, kv, "bf16", seed=41)
-    dev = DeviceInputs(build_host_inputs(w))
-    a = from_dev(dev.decode(partition_tokens=P, kernel=2))
-    b = from_dev(dev.decode(partition_tokens=P, kernel=3))
-    assert np.array_equal(a, b)
-
-
-def test_repeated_calls_on_one_workspace():
-    """Repeated calls on one workspace give identical results."""
+def _two_stage(dev, P, kernel=2):
+    """pa_decode_partition then pa_merge: the pieces always go through the workspace."""
     import torch
     import paged_kv_cache_112_amd as pa
-    w = custom_workload([300, 17, 1500, 64, 0, 999], 32, 8, 128, 16, "bf16", "bf16", seed=43)
+    h, w = dev.h, dev.h.w
+    out, ws = pa.decode_partition(dev.q, dev.kc, dev.vc, dev.bt, dev.ctx, w.scale, max_context_len=dev.max_ctx,
+                                  partition_tokens=P, kernel=kernel, k_scale=h.k_scale, v_scale=h.v_scale)
+    if ws is not None:
+        pa.merge(ws, dev.ctx, out, dev.max_ctx, P)
+    torch.cuda.synchronize()
+    return out
+
+
+@pytest.mark.parametrize("kv", ["bf16", "e4m3", "i8"])
+@pytest.mark.parametrize("P,ctx_extra", [(16, [100, 255]), (64, [1000, 1024]), (128, [1000, 2047]),
+                                         (256, [1000, 2047, 4096]), (256, [4097]), (512, [3000])])
+def test_decode_equals_its_two_stages_bitwise(P, ctx_extra, kv):
+    """pa_decode is pa_decode_partition then pa_merge, bit for bit, whichever merge schedule the
+    partition count picks (one 16-lane row per head up to 16 partitions, the partition-parallel
+    one beyond), and agrees with the oracle."""
+    w = custom_workload(EDGE_CTX + ctx_extra, 32, 8, 128, 16, kv, "bf16", seed=41 + P)
     h = build_host_inputs(w)
     dev = DeviceInputs(h)
-    ws = pa.new_workspace(w.num_seqs, 32, 128, dev.max_ctx, 64)
-    outs = []
-    for _ in range(4):
-        res = pa.decode(dev.q, dev.kc, dev.vc, dev.bt, dev.ctx, w.scale, max_context_len=dev.max_ctx,
-                        workspace=ws, partition_tokens=64, kernel=3)
+    a = dev.decode(partition_tokens=P, kernel=2)
+    b = _two_stage(dev, P)
+    assert np.array_equal(from_dev(a), from_dev(b))
+    assert np.abs(out_to_f64(a) - h.oracle_decode()).max() <= TOL[kv]
+
+
+@pytest.mark.parametrize("P", [64, 256])
+def test_repeated_calls_on_one_workspace(P):
+    """Calls on one workspace, with the contexts changing between them (as a decode loop's do):
+    every result matches the oracle."""
+    import torch
+    import paged_kv_cache_112_amd as pa
+    base = [300, 17, 1500, 64, 0, 999, 1024, 257]
+    w0 = custom_workload(base, 32, 8, 128, 16, "bf16", "bf16", seed=43)
+    h = build_host_inputs(w0)
+    dev = DeviceInputs(h)
+    max_ctx = dev.max_ctx
+    ws = pa.new_workspace(w0.num_seqs, 32, 128, max_ctx, P)
+    for step, cut in enumerate([0, 0, 5, 200, 1, 0]):
+        ctx = np.maximum(np.array(base) - cut * (np.arange(len(base)) % 3), 0).astype(np.int32)
+        print(f"step {step} P={P} ctx={ctx.tolist()}", flush=True)
+        res = pa.decode(dev.q, dev.kc, dev.vc, dev.bt, to_dev(ctx), w0.scale, max_context_len=max_ctx,
+                        workspace=ws, partition_tokens=P, kernel=2)
         torch.cuda.synchronize()
-        outs.append(from_dev(res))
-    for o in outs[1:]:
-        assert np.array_equal(o, outs[0])
-    assert np.abs(out_to_f64(res) - h.oracle_decode()).max() <= 2e-2
+        ref = oracle.decode(h.q, h.kc, h.vc, w0.block_tables, ctx, w0.scale, "bf16", "bf16")
+        assert np.abs(out_to_f64(res) - ref).max() <= 2e-2, step
+
+
+def test_decode_graph_replays_with_eager_calls_between():
+    """pa_decode captured in a HIP graph and replayed, with eager calls on the same workspace
+    between the replays: every replay gives the eager bits."""
+    import torch
+    import paged_kv_cache_112_amd as pa
+    w = custom_workload([3000, 17, 1500, 256, 257, 2048, 4000], 32, 8, 128, 16, "bf16", "bf16", seed=45)
+    h = build_host_inputs(w)
+    dev = DeviceInputs(h)
+    ws = pa.new_workspace(w.num_seqs, 32, 128, dev.max_ctx, 0)
+    out = torch.empty_like(dev.q)
+    eager = from_dev(pa.decode(dev.q, dev.kc, dev.vc, dev.bt, dev.ctx, w.scale, max_context_len=dev.max_ctx,
+                               workspace=ws))
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            pa.decode(dev.q, dev.kc, dev.vc, dev.bt, dev.ctx, w.scale, out=out, max_context_len=dev.max_ctx,
+                      workspace=ws, stream=side.cuda_stream)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    for i in range(5):
+        out.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(from_dev(out), eager), i
+        again = pa.decode(dev.q, dev.kc, dev.vc, dev.bt, dev.ctx, w.scale, max_context_len=dev.max_ctx, workspace=ws)
+        torch.cuda.synchronize()
+        assert np.array_equal(from_dev(again), eager), i
+    assert np.abs(out_to_f64(out) - h.oracle_decode()).max() <= 2e-2
+
+
+def test_context_beyond_max_context_len_stays_in_bounds():
+    """A context longer than the launch's max_context_len breaks the caller contract; the launch
+    then covers only its first ceil(max_context_len / P) partitions and writes nowhere else:
+    the other sequences' outputs are still right and guard bytes around the workspace keep
+    their values."""
+    import torch
+    import paged_kv_cache_112_amd as pa
+    ctx = [1000, 600, 300, 45]
+    w = custom_workload(ctx, 32, 8, 128, 16, "bf16", "bf16", seed=49)
+    h = build_host_inputs(w)
+    dev = DeviceInputs(h)
+    lied = 512                     # sequence 0 has 1000 tokens, sequence 1 600
+    ref = h.oracle_decode()
+    for P in (64, 256):
+        need = pa.decode_workspace_bytes(4, 32, 128, lied, P)
+        guard = 4096
+        buf = torch.full((need + 2 * guard,), 0xA5, dtype=torch.uint8, device="cuda")
+        ws = buf[guard:guard + need]
+        ws.zero_()
+        print(f"max_context_len {lied} below the longest context, P={P}", flush=True)
+        res = pa.decode(dev.q, dev.kc, dev.vc, dev.bt, dev.ctx, w.scale, max_context_len=lied, workspace=ws,
+                        partition_tokens=P, kernel=2)
+        torch.cuda.synchronize()
+        got = out_to_f64(res)
+        assert np.abs(got[2:] - ref[2:]).max() <= 2e-2
+        assert (buf[:guard].cpu().numpy() == 0xA5).all() and (buf[guard + need:].cpu().numpy() == 0xA5).all()
 
 
 _MANY = {}
@@ -234,12 +315,12 @@ def _many_sequences(B, kv):
     return _MANY[(B, kv)]
 
 
-@pytest.mark.parametrize("kernel", [2, 3])
+@pytest.mark.parametrize("kernel", [1, 2])
 @pytest.mark.parametrize("P", [64, 256])
 @pytest.mark.parametrize("B,kv", [(65, "bf16"), (777, "bf16"), (777, "e4m3"), (1024, "bf16")])
 def test_dense_numbering_over_many_sequence_chunks(B, kv, P, kernel):
-    """Between 65 and 1024 sequences both matrix-core schedules still number only existing
-    pairs, scanning the context lengths 64 at a time: every chunk boundary is crossed."""
+    """Between 65 and 1024 sequences both partition kernels still number only existing pairs,
+    scanning the context lengths 64 at a time: every chunk boundary is crossed."""
     w, h, ref = _many_sequences(B, kv)
     print(f"decode {B} sequences kv={kv} P={P} kernel={kernel}", flush=True)
     out = out_to_f64(DeviceInputs(h).decode(P, kernel))
@@ -247,11 +328,14 @@ def test_dense_numbering_over_many_sequence_chunks(B, kv, P, kernel):
     assert np.abs(out - ref).max() <= TOL[kv]
 
 
-def test_large_batch_falls_back_to_grid_kernel():
-    """More sequences than the persistent kernel's running total holds: the grid kernel runs instead."""
+@pytest.mark.parametrize("P", [32, 16])
+def test_more_sequences_than_the_dense_numbering(P):
+    """1,100 sequences: beyond the in-kernel numbering the grid is (partitions x sequences); with
+    P = 32 a sequence has at most 3 partitions, with P = 16 at most 6, and both merge in the
+    partition launch."""
     ctx = [1 + (7 * i) % 90 for i in range(1100)]
     w = custom_workload(ctx, 8, 2, 64, 16, "bf16", "bf16", seed=47)
-    _check(DeviceInputs(build_host_inputs(w)), w, partition_tokens=32, kernel=3)
+    _check(DeviceInputs(build_host_inputs(w)), w, partition_tokens=P, kernel=2)
 
 
 # ---------------------------------------------------------------------------
