@@ -23,14 +23,20 @@ def _run(kc0, vc0, k, v, slots, kv_fmt, in_fmt, ks=1.0, vs=1.0):
 
 def _random_pool(shape, fmt, seed):
     """Pool bytes that are random (not zero), so an untouched slot is checked too."""
-    raw = np.random.default_rng(seed).integers(0, 256, size=int(np.prod(shape)) * np.dtype(STORAGE[fmt]).itemsize,
-                                               dtype=np.uint8)
-    return raw.view(STORAGE[fmt]).reshape(shape)
+    n = int(np.prod(shape)) * np.dtype(STORAGE[fmt]).itemsize
+    raw = np.frombuffer(np.random.default_rng(seed).bytes(n), dtype=np.uint8)
+    return raw.view(STORAGE[fmt]).reshape(shape).copy()
 
 
-@pytest.mark.parametrize("name", ["tiny_f32", "llama3_8b_b64", "llama3_8b_fp8_prefix"])
-def test_append_step_bit_exact(name):
-    w = make_config(name)
+# every workload, the MHA one at each of its block sizes
+WORKLOADS = [("tiny_f32", None), ("llama3_8b_b64", None), ("llama3_8b_long", None), ("llama2_7b_mha", 1),
+             ("llama2_7b_mha", 16), ("llama2_7b_mha", 64), ("llama2_7b_mha", 256), ("llama3_8b_fp8_prefix", None)]
+
+
+@pytest.mark.parametrize("name,bs", WORKLOADS)
+def test_append_step_bit_exact(name, bs):
+    """The decode step's write (position ctx - 1 of every sequence) into random pools: whole pools equal."""
+    w = make_config(name, bs)
     shape = (w.num_blocks, w.block_size, w.num_kv_heads, w.head_dim)
     k, v, in_fmt, slots = append_step(w)
     ks, vs = (0.0137, 0.0119) if w.kv_dtype == "e4m3" else (1.0, 1.0)
@@ -38,6 +44,24 @@ def test_append_step_bit_exact(name):
     got_k, got_v, ref_k, ref_v = _run(pool, pool.copy(), k, v, slots, w.kv_dtype, in_fmt, ks, vs)
     assert np.array_equal(got_k.view(np.uint8), ref_k.view(np.uint8))
     assert np.array_equal(got_v.view(np.uint8), ref_v.view(np.uint8))
+
+
+@pytest.mark.parametrize("name,bs", [("llama3_8b_long", None), ("llama2_7b_mha", 1), ("llama2_7b_mha", 16),
+                                     ("llama2_7b_mha", 64), ("llama2_7b_mha", 256)])
+def test_prefill_shaped_write_every_context_token(name, bs):
+    """Every context token of the workload in one call (524,288 rows of 2 KiB for the 8192-token
+    batch; 63,638 rows of 8 KiB for the MHA layer): whole pools equal the oracle's, bit for bit."""
+    w = make_config(name, bs)
+    slots = np.concatenate([w.slots(b, w.owned_positions(b)) for b in range(w.num_seqs)]).astype(np.int32)
+    n = len(slots)
+    assert n == w.total_tokens
+    rng = np.random.default_rng(5)
+    k = rng.integers(0, 1 << 16, (n, w.num_kv_heads, w.head_dim), dtype=np.uint16)
+    v = rng.integers(0, 1 << 16, (n, w.num_kv_heads, w.head_dim), dtype=np.uint16)
+    shape = (w.num_blocks, w.block_size, w.num_kv_heads, w.head_dim)
+    pool = np.full(shape, 0x7FC0, dtype=np.uint16)
+    got_k, got_v, ref_k, ref_v = _run(pool, pool.copy(), k, v, slots, "bf16", "bf16")
+    assert np.array_equal(got_k, ref_k) and np.array_equal(got_v, ref_v)
 
 
 def test_prefill_shaped_write_llama3():
