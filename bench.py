@@ -4,15 +4,18 @@ Workload: one Llama-3-8B attention layer (32 query heads, 8 KV heads, head dim
 128, bf16), batch 64, block size 16, context lengths = prompt U[100,2000] +
 output U[20,1500] from the seeded generator, physical blocks shuffled over a
 pool 10 % larger than needed.  One step is the whole hot path for one batch:
-pa_write_kv of this step's 64 tokens, then pa_decode (partition kernel + merge);
-with --fused the partition kernel writes the tokens itself
-(pa_decode_partition_append).
+pa_write_kv of this step's 64 tokens, then pa_decode (the partition kernel, which
+also merges the split-K pieces in its last workgroup of each sequence); with
+--fused the decode launch writes the tokens itself (pa_decode_append).
 Each step uses the next of L layer-pool copies, as a model's layers would, so
-the 256 MB MALL cannot serve a pool read by an earlier step.
+the 256 MB MALL cannot serve a pool read by an earlier step (the same effect as
+flushing it before each step).
 
 Prints one JSON line: value = algorithmic bytes of the step / step time (GB/s);
-roofline = the partition kernel (the dominant one) against HBM peak, timed
-live with HIP events on the stream it runs on; cpu_baseline = the CPU oracle.
+roofline = pa_decode (partition + merge, the dominant launch) against HBM peak,
+timed live with HIP events on the stream it runs on; contiguous = the same decode
+over identity-ordered block tables; cpu_baseline = the CPU oracle on all host cores
+and on one.
 """
 from __future__ import annotations
 
@@ -32,9 +35,10 @@ sys.path.insert(0, ROOT)
 WORKLOAD = "llama3_8b_b64"
 HBM_PEAK_GBS = 8000.0
 LAYERS = 8
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_partition_llama3_8b_b64.traffic.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_mfma_llama3_8b_b64.traffic.json")
 KERNEL_SOURCES = ["paged_kv_cache_112_amd/csrc/decode_mfma.hip", "paged_kv_cache_112_amd/csrc/common.hpp",
-                  "paged_kv_cache_112_amd/csrc/mfma_tiles.hpp", "paged_kv_cache_112_amd/csrc/launch.hpp"]
+                  "paged_kv_cache_112_amd/csrc/mfma_tiles.hpp", "paged_kv_cache_112_amd/csrc/launch.hpp",
+                  "paged_kv_cache_112_amd/csrc/merge_rows.hpp"]
 
 
 def algorithmic_bytes(w, kv_bytes=2, q_bytes=2, out_bytes=2, in_bytes=2):
@@ -64,7 +68,7 @@ def kernel_sha() -> str:
 
 
 def measured_traffic():
-    """HBM bytes per partition-kernel launch from the committed rocprofv3 counter runs, if still current."""
+    """HBM bytes per pa_decode launch from the committed rocprofv3 counter runs, if still current."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
@@ -75,10 +79,29 @@ def measured_traffic():
     return t.get("bytes_per_launch")
 
 
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _host_cores() -> int:
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:
+        return os.cpu_count() or 1
+
+
 def cpu_baseline(w):
-    """The oracle, as it stands, on the same decode workload (all 64 sequences), on host cores."""
+    """The oracle, as it stands, on the same decode workload (all 64 sequences): once with every
+    host core its BLAS may use, once on one core; median of a few runs each (about 10-20 s)."""
     import oracle
-    from threadpoolctl import threadpool_limits
+    from threadpoolctl import threadpool_info, threadpool_limits
     from workloads import f32_to_bf16_bits
 
     shape = (w.num_blocks, w.block_size, w.num_kv_heads, w.head_dim)
@@ -89,21 +112,31 @@ def cpu_baseline(w):
         oracle.write_kv(kc, vc, f32_to_bf16_bits(w.seq_token_values("k", b)),
                         f32_to_bf16_bits(w.seq_token_values("v", b)), w.slots(b, pos), "bf16", "bf16")
     q = f32_to_bf16_bits(w.q_values())
-    times = []
-    with threadpool_limits(limits=1):
-        deadline = time.perf_counter() + 20.0
-        while len(times) < 3 or (time.perf_counter() < deadline and len(times) < 10):
-            t0 = time.perf_counter()
-            oracle.decode(q, kc, vc, w.block_tables, w.context_lens, w.scale, "bf16", "bf16")
-            times.append(time.perf_counter() - t0)
-            if sum(times) > 30.0:
-                break
-    t = statistics.median(times)
     nbytes = algorithmic_bytes(w)["decode"]
-    return {"value": round(nbytes / t / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "tokens_per_s": round(w.num_seqs / t, 2), "seconds_per_decode": round(t, 4),
-            "sample": f"full {WORKLOAD} decode (64 sequences, sum ctx {w.total_tokens}), fp64 numpy, "
-                      f"one thread, median of {len(times)} runs"}
+    cores = _host_cores()
+
+    def timed(limit):
+        times = []
+        with threadpool_limits(limits=limit):
+            used = max([int(i.get("num_threads", 1)) for i in threadpool_info()] or [1])
+            deadline = time.perf_counter() + 10.0
+            while len(times) < 3 or (time.perf_counter() < deadline and len(times) < 10):
+                t0 = time.perf_counter()
+                oracle.decode(q, kc, vc, w.block_tables, w.context_lens, w.scale, "bf16", "bf16")
+                times.append(time.perf_counter() - t0)
+        t = statistics.median(times)
+        return t, used, len(times)
+
+    t_all, used_all, n_all = timed(cores)
+    t_one, _, n_one = timed(1)
+    return {"value": round(nbytes / t_all / 1e9, 4), "unit": "GB/s", "cores": used_all, "kind": "oracle",
+            "tokens_per_s": round(w.num_seqs / t_all, 2), "seconds_per_decode": round(t_all, 4),
+            "one_core": {"value": round(nbytes / t_one / 1e9, 4), "unit": "GB/s", "cores": 1,
+                         "tokens_per_s": round(w.num_seqs / t_one, 2), "seconds_per_decode": round(t_one, 4)},
+            "nproc": cores, "cpu_model": _cpu_model(),
+            "sample": f"full {WORKLOAD} decode (64 sequences, sum ctx {w.total_tokens}), fp64 numpy oracle; "
+                      f"BLAS threads limited to the host's {cores} cores (median of {n_all} runs) and to one "
+                      f"(median of {n_one})"}
 
 
 def _time_launches(torch, fn, reps, warmup):
@@ -328,7 +361,9 @@ def bench_graph_loop(args, torch, pa):
     steps = max(args.steps, 8) // LAYERS * LAYERS
     warm = max(args.warmup, 1)
     B, hq, hkv, d, bs = w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim, w.block_size
-    room = (steps + warm) // LAYERS + 2                      # tokens each sequence gains
+    reps = steps // LAYERS
+    # every replay of the graph (warmup included) is one model step: one more token per sequence
+    room = warm + reps + 2
     final = w.context_lens + room
     need = int(sum(-(-int(c) // bs) for c in final))
     nb = int(np.ceil(1.1 * need))
@@ -369,13 +404,16 @@ def bench_graph_loop(args, torch, pa):
     torch.cuda.synchronize()
     s = torch.cuda.current_stream()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    reps = steps // LAYERS
     e0.record(s)
     for _ in range(reps):
         graph.replay()
     e1.record(s)
     torch.cuda.synchronize()
     us_layer = e0.elapsed_time(e1) * 1e3 / (reps * LAYERS)
+    # the tables were sized for the growth: no length may have passed them
+    grown = ctx.cpu().numpy()
+    if not (grown == w.context_lens - 1 + warm + reps).all() or (grown > final).any():
+        raise SystemExit("graph loop: context lengths outgrew the block tables")
     print(json.dumps({"metric": "device-side decode loop (slot mapping + write + decode per layer, graph replay)",
                       "workload": WORKLOAD, "fused_write": bool(args.fused), "layers_per_graph": LAYERS,
                       "model_steps": reps,
@@ -390,8 +428,11 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--partition", type=int, default=0, help="partition tokens (0 = library default)")
-    ap.add_argument("--kernel", type=int, default=0, help="0 auto, 1 vector path, 2 matrix-core, 3 matrix-core persistent")
+    ap.add_argument("--kernel", type=int, default=0, help="0 auto, 1 vector path, 2 matrix-core")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-contiguous", action="store_true", help="skip the identity-table comparator")
+    ap.add_argument("--two-launch", action="store_true",
+                    help="decode as pa_decode_partition + pa_merge (two launches) instead of pa_decode")
     ap.add_argument("--workload", default=WORKLOAD,
                     choices=["llama3_8b_b64", "llama3_8b_long", "llama2_7b_mha", "llama3_8b_fp8_prefix"])
     ap.add_argument("--block-size", type=int, default=None, help="block size for llama2_7b_mha")
@@ -407,8 +448,8 @@ def main():
                          "loop with device-side slot mapping, captured once and replayed; stream_read: a plain "
                          "streaming read of the same byte count, the practical HBM ceiling")
     ap.add_argument("--fused", action="store_true",
-                    help="the step's write done by the partition launch itself (pa_decode_partition_append + "
-                         "pa_merge) instead of pa_write_kv + pa_decode_partition + pa_merge")
+                    help="the step's write done by the decode launch itself (pa_decode_append) instead of "
+                         "pa_write_kv + pa_decode")
     ap.add_argument("--contiguous", action="store_true",
                     help="identity-ordered block tables (each sequence's blocks adjacent): the contiguous comparator")
     args = ap.parse_args()
@@ -465,17 +506,31 @@ def main():
     qmax = 448.0 if w.kv_dtype == "e4m3" else 127.0
     k_scale, v_scale = (float(np.float32(4.8 / qmax)), float(np.float32(4.8 / qmax))) if fp8 else (1.0, 1.0)
     shape = (w.num_blocks, bs, hkv, d)
-    k0 = torch.zeros(shape, dtype=kv_dtype, device=dev)
-    v0 = torch.zeros(shape, dtype=kv_dtype, device=dev)
+
+    def fill_pools(tables):
+        """LAYERS copies of the pools, [LAYERS, num_blocks, bs, H_kv, d] per K and V, holding every
+        context token but this step's at the slots ``tables`` give; the same values for any tables."""
+        k0 = torch.zeros(shape, dtype=kv_dtype, device=dev)
+        v0 = torch.zeros(shape, dtype=kv_dtype, device=dev)
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(w.seed)
+        for b in range(B):
+            pos = w.owned_positions(b)[:-1]
+            if len(pos) == 0:
+                continue
+            K = torch.randn((len(pos), hkv, d), generator=gen, device=dev).to(torch.bfloat16)
+            V = torch.randn((len(pos), hkv, d), generator=gen, device=dev).to(torch.bfloat16)
+            sl = (tables[b, pos // bs].astype(np.int64) * bs + pos % bs).astype(np.int32)
+            pa.write_kv(K, V, to_dev(sl), k0, v0, k_scale, v_scale)
+        k_all = k0.unsqueeze(0).repeat(LAYERS, 1, 1, 1, 1)
+        v_all = v0.unsqueeze(0).repeat(LAYERS, 1, 1, 1, 1)
+        del k0, v0
+        return k_all, v_all
+
+    k_all, v_all = fill_pools(w.block_tables)
+    pools = [(k_all[l], v_all[l]) for l in range(LAYERS)]
     gen = torch.Generator(device=dev)
-    gen.manual_seed(w.seed)
-    for b in range(B):
-        pos = w.owned_positions(b)[:-1]
-        if len(pos) == 0:
-            continue
-        K = torch.randn((len(pos), hkv, d), generator=gen, device=dev).to(torch.bfloat16)
-        V = torch.randn((len(pos), hkv, d), generator=gen, device=dev).to(torch.bfloat16)
-        pa.write_kv(K, V, to_dev(w.slots(b, pos).astype(np.int32)), k0, v0, k_scale, v_scale)
+    gen.manual_seed(w.seed + 1)
     k_new = torch.randn((B, hkv, d), generator=gen, device=dev).to(torch.bfloat16)
     v_new = torch.randn((B, hkv, d), generator=gen, device=dev).to(torch.bfloat16)
     slots = to_dev(w.append_slots())
@@ -483,11 +538,6 @@ def main():
     bt = to_dev(w.block_tables)
     ctx = to_dev(w.context_lens)
     max_ctx = int(w.context_lens.max())
-    # the layers' pools as one allocation per K and V, [LAYERS, num_blocks, bs, H_kv, d], used by layer view
-    k_all = k0.unsqueeze(0).repeat(LAYERS, 1, 1, 1, 1)
-    v_all = v0.unsqueeze(0).repeat(LAYERS, 1, 1, 1, 1)
-    del k0, v0
-    pools = [(k_all[l], v_all[l]) for l in range(LAYERS)]
     out = torch.empty((B, hq, d), dtype=torch.bfloat16, device=dev)
     P = args.partition or pa.pa_default_partition_tokens()
     ws = pa.new_workspace(B, hq, d, max_ctx, P, dev)
@@ -497,32 +547,27 @@ def main():
 
     stream = torch.cuda.current_stream()
 
-    # --fused: the step's write is done by the partition launch itself (matrix-core grid
-    # kernel, partitions of 256 tokens or more)
+    # --fused: the step's write is done by the decode launch itself (matrix-core grid kernel,
+    # partitions of 256 tokens or more)
     fused = args.fused and args.kernel in (0, 2) and P >= 256 and w.kv_dtype != "f32"
 
-    def partition(kc, vc):
+    def decode(kc, vc, tables=bt):
         if fused:
-            pa.decode_partition_append(q, k_new, v_new, kc, vc, bt, ctx, w.scale, out=out, max_context_len=max_ctx,
-                                       workspace=ws, partition_tokens=P, k_scale=k_scale, v_scale=v_scale)
-        else:
-            pa.decode_partition(q, kc, vc, bt, ctx, w.scale, out=out, max_context_len=max_ctx, workspace=ws,
+            pa.decode_append(q, k_new, v_new, kc, vc, tables, ctx, w.scale, out=out, max_context_len=max_ctx,
+                             workspace=ws, partition_tokens=P, k_scale=k_scale, v_scale=v_scale)
+        elif args.two_launch:
+            pa.decode_partition(q, kc, vc, tables, ctx, w.scale, out=out, max_context_len=max_ctx, workspace=ws,
                                 partition_tokens=P, kernel=args.kernel, k_scale=k_scale, v_scale=v_scale)
+            pa.merge(ws, ctx, out, max_ctx, P)
+        else:
+            pa.decode(q, kc, vc, tables, ctx, w.scale, out=out, max_context_len=max_ctx, workspace=ws,
+                      partition_tokens=P, kernel=args.kernel, k_scale=k_scale, v_scale=v_scale)
 
-    def step(i, ev=None):
+    def step(i):
         kc, vc = pools[i % LAYERS]
-        if ev is not None:
-            ev[0].record(stream)
         if not fused:
             pa.write_kv(k_new, v_new, slots, kc, vc, k_scale, v_scale)
-        if ev is not None:
-            ev[1].record(stream)
-        partition(kc, vc)
-        if ev is not None:
-            ev[2].record(stream)
-        pa.merge(ws, ctx, out, max_ctx, P)
-        if ev is not None:
-            ev[3].record(stream)
+        decode(kc, vc)
 
     for i in range(args.warmup):
         step(i)
@@ -533,19 +578,18 @@ def main():
     # forward pass would replay them); replays cost no per-kernel host work --------------------
     side = torch.cuda.Stream()
     side.wait_stream(stream)
-    graphs = []
-    with torch.cuda.stream(side):
-        for i in range(LAYERS):
-            g = torch.cuda.CUDAGraph()
+
+    def capture(fn):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(side):
             with torch.cuda.graph(g, stream=side):
-                step(i)
-            graphs.append(g)
-        all_layers = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(all_layers, stream=side):
-            for i in range(LAYERS):
-                step(i)
-    stream.wait_stream(side)
-    torch.cuda.synchronize()
+                fn()
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        return g
+
+    graphs = [capture(lambda i=i: step(i)) for i in range(LAYERS)]
+    all_layers = capture(lambda: [step(i) for i in range(LAYERS)])
     for i, g in enumerate(graphs + [all_layers]):   # every replay must reproduce the eager result exactly
         out.zero_()
         g.replay()
@@ -566,46 +610,74 @@ def main():
     torch.cuda.synchronize()
     ms_per_step = t_start.elapsed_time(t_end) / args.steps
 
-    # ---- the dominant kernel alone: back-to-back launches between two events --------------------
-    part_graph = torch.cuda.CUDAGraph()
-    with torch.cuda.stream(side):
-        with torch.cuda.graph(part_graph, stream=side):
-            for i in range(LAYERS):
-                partition(*pools[i])
-    stream.wait_stream(side)
+    # ---- the step's distribution: each replay of the 8-layer graph between its own two events
+    # (per step = replay / 8; a pair of events per single step would add its own overhead) ------
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(max(2, args.steps // LAYERS))]
     torch.cuda.synchronize()
-    reps = max(1, args.steps // LAYERS)
-    p_start = torch.cuda.Event(enable_timing=True)
-    p_end = torch.cuda.Event(enable_timing=True)
-    p_start.record(stream)
-    for _ in range(reps):
-        part_graph.replay()
-    p_end.record(stream)
+    for e0, e1 in evs:
+        e0.record(stream)
+        all_layers.replay()
+        e1.record(stream)
     torch.cuda.synchronize()
-    part_launch_ms = p_start.elapsed_time(p_end) / (reps * LAYERS)
+    per_step_us = sorted(e0.elapsed_time(e1) * 1e3 / LAYERS for e0, e1 in evs)
 
-    # ---- per-kernel durations: HIP events on the library's stream, queue kept full ------------
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    try:
-        torch.cuda._sleep(200_000_000)           # GPU busy while the host enqueues every step
-    except (AttributeError, RuntimeError):
-        pass
-    for i in range(args.steps):
-        step(i, evs[i])
-    torch.cuda.synchronize()
-    write_ms = statistics.mean(e[0].elapsed_time(e[1]) for e in evs)
-    part_ms = statistics.mean(e[1].elapsed_time(e[2]) for e in evs)
-    merge_ms = statistics.mean(e[2].elapsed_time(e[3]) for e in evs)
-    eager_ms = (evs[0][0].elapsed_time(evs[-1][3])) / max(1, args.steps - 1) if args.steps > 1 else None
+    def pct(xs, p):
+        return round(float(np.percentile(np.asarray(xs), p)), 2)
+
+    # ---- pa_decode alone (partition + merge, the dominant launch): back-to-back graph replays ---
+    def time_decode(tables, layer_pools):
+        g = capture(lambda: [decode(*layer_pools[i], tables) for i in range(LAYERS)])
+        g.replay()
+        torch.cuda.synchronize()
+        reps = max(2, args.steps // LAYERS)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        # per-replay spread: each replay of 8 launches between its own events
+        spread = []
+        for _ in range(reps):
+            a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a0.record(stream)
+            g.replay()
+            a1.record(stream)
+            spread.append((a0, a1))
+        torch.cuda.synchronize()
+        per = sorted(a0.elapsed_time(a1) * 1e3 / LAYERS for a0, a1 in spread)
+        return e0.elapsed_time(e1) * 1e3 / (reps * LAYERS), per
+
+    decode_us, decode_spread = time_decode(bt, pools)
 
     nb = algorithmic_bytes(w, kv_bytes=1 if fp8 else 2)
     value = nb["step"] / (ms_per_step * 1e-3) / 1e9
-    launch_bytes = nb["partition_append"] if fused else nb["partition"]
-    achieved = launch_bytes / (part_launch_ms * 1e-3) / 1e9
+    launch_bytes = nb["step"] if fused else nb["decode"]
+    achieved = launch_bytes / (decode_us * 1e-6) / 1e9
     # the committed counter run covers the default launch of the headline workload only
     default_launch = (w.name == WORKLOAD and P == 256 and args.kernel in (0, 2) and not args.contiguous and not fused)
     traffic = measured_traffic() if default_launch else None
+
+    # ---- the contiguous comparator: the same tokens and lengths, each sequence's blocks adjacent
+    contiguous = None
+    if not args.no_contiguous:
+        from workloads import deal_tables
+        ident, _ = deal_tables(w.context_lens, bs, np.arange(w.num_blocks, dtype=np.int32))
+        del pools
+        k_all = v_all = None
+        torch.cuda.synchronize()
+        ck_all, cv_all = fill_pools(ident)
+        cpools = [(ck_all[l], cv_all[l]) for l in range(LAYERS)]
+        bt_ident = to_dev(ident)
+        c_us, c_spread = time_decode(bt_ident, cpools)
+        contiguous = {"block_order": "identity (each sequence's blocks adjacent, in order)",
+                      "decode_us": round(c_us, 2), "GB/s": round(launch_bytes / (c_us * 1e-6) / 1e9, 1),
+                      "frac": round(launch_bytes / (c_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                      "decode_us_median": pct(c_spread, 50),
+                      "paged_over_contiguous_time": round(decode_us / c_us, 4)}
+        del cpools, ck_all, cv_all
+
     result = {
         "metric": "paged-attn decode achieved HBM GB/s + tokens/s, Llama-3-8B layer, batch 64",
         "value": round(value, 2),
@@ -616,6 +688,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 5),
+        "step_us_median": pct(per_step_us, 50), "step_us_p10": pct(per_step_us, 10),
+        "step_us_p90": pct(per_step_us, 90),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -623,28 +697,30 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "batch": B, "num_q_heads": hq, "num_kv_heads": hkv, "head_dim": d,
                    "block_size": bs, "sum_context": w.total_tokens, "max_context": max_ctx,
-                   "partition_tokens": P, "kernel": ["auto", "valu", "mfma", "mfma_persist"][args.kernel],
+                   "partition_tokens": P, "kernel": ["auto", "valu", "mfma"][args.kernel],
                    "layer_pools_rotated": LAYERS,
-                   "step": ("pa_decode_partition_append (writes the 64 new tokens, then decodes) + pa_merge"
-                            if fused else "pa_write_kv(64 tokens) + pa_decode_partition + pa_merge"),
+                   "step": ("pa_decode_append (writes the 64 new tokens, decodes, merges)" if fused
+                            else "pa_write_kv(64 tokens) + pa_decode_partition + pa_merge" if args.two_launch
+                            else "pa_write_kv(64 tokens) + pa_decode"),
                    "block_order": "identity (contiguous comparator)" if args.contiguous else "seeded permutation"},
-        "kernel_us": {"write_kv": round(write_ms * 1e3, 2) if not fused else 0.0,
-                      "decode_partition": round(part_ms * 1e3, 2),
-                      "merge": round(merge_ms * 1e3, 2)},
-        "decode_partition_us_back_to_back": round(part_launch_ms * 1e3, 2),
-        "timing": "steps replayed from a HIP graph of the 8 layer steps; kernel_us: HIP events around each "
-                  "eager launch queued behind a busy GPU (each pair adds a few us); roofline: HIP events "
-                  "around back-to-back replays of the partition kernel alone",
-        "eager_ms_per_step": round(eager_ms, 5) if eager_ms else None,
+        "pa_decode": {"us": round(decode_us, 2), "us_median": pct(decode_spread, 50),
+                      "us_p10": pct(decode_spread, 10), "us_p90": pct(decode_spread, 90),
+                      "GB/s": round(achieved, 1), "tokens_per_s": round(B / (decode_us * 1e-6), 1),
+                      "kv_tokens_per_s": round(w.total_tokens / (decode_us * 1e-6), 1)},
+        "timing": "value/ms_per_step: K steps replayed from HIP graphs of the 8 layer steps between two events; "
+                  "step_us_*: percentiles over replays of the 8-step graph, each between its own events, per "
+                  "step; pa_decode: back-to-back replays of a graph of 8 pa_decode calls (one per layer pool), "
+                  "HIP events on the launch stream, percentiles per replay",
         "bytes": nb,
         "roofline": {"bound": "hbm",
-                     "kernel": ("decode_mfma_kernel (partition stage, appending the step's tokens)" if fused
-                                else "decode_mfma_kernel (partition stage)"),
+                     "kernel": ("pa_decode_append: decode_mfma_kernel (write + partition stage) + merge kernel"
+                                if fused else "pa_decode: decode_mfma_kernel (partition stage) + merge kernel"),
                      "bytes_per_launch": launch_bytes,
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic},
+        "contiguous": contiguous,
     }
-    if not args.no_cpu_baseline and args.workload == WORKLOAD:
+    if not args.no_cpu_baseline and args.workload == WORKLOAD and not args.kv_dtype:
         result["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(result))
 
