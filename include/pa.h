@@ -19,8 +19,10 @@
  * Conventions for every call:
  *   - Pointers named as device data are device pointers (hipMalloc / torch CUDA
  *     tensors) owned by the caller; arrays are row-major and contiguous.  The
- *     library never allocates, frees or keeps device memory, and keeps no
- *     state between calls; calls are thread-safe.
+ *     library never allocates or frees device memory and keeps no state between
+ *     calls, except pa_decode_noalloc's static scratch array (64 MiB on each GPU
+ *     the library's code is loaded on); calls are thread-safe, bar the overlap
+ *     rule of pa_decode_noalloc.
  *   - `stream` is a hipStream_t (NULL = the null stream).  Calls only enqueue
  *     work: no host synchronization, no allocation, so they can be captured in
  *     a HIP graph.
@@ -57,7 +59,8 @@ typedef enum pa_status {
   PA_ERR_DTYPE = 3,       /* unsupported dtype or dtype combination */
   PA_ERR_UNSUPPORTED = 4, /* supported dtypes, unsupported head_dim / block_size / partition size */
   PA_ERR_WORKSPACE = 5,   /* workspace missing or smaller than pa_decode_workspace_bytes() */
-  PA_ERR_HIP = 6          /* the HIP runtime reported an error when launching */
+  PA_ERR_HIP = 6,         /* the HIP runtime reported an error when launching */
+  PA_ERR_SCRATCH = 7      /* pa_decode_noalloc: the shape needs more than the static scratch */
 } pa_status;
 
 typedef enum pa_dtype {
@@ -208,6 +211,28 @@ pa_status pa_decode(const void* q, int32_t q_dtype, int32_t num_seqs, int32_t nu
                     const int32_t* context_lens, int32_t max_context_len, float scale,
                     void* out, void* workspace, size_t workspace_bytes,
                     int32_t partition_tokens, int32_t kernel, void* stream);
+
+/* pa_decode for callers that cannot allocate: code under HIP graph capture, tight serving
+ * loops, or harnesses that forbid device allocation.  Same arguments and results as
+ * pa_decode (bit for bit) minus the workspace: the split-K pieces live in a static
+ * device array of the library, PA_DECODE_NOALLOC_SCRATCH_BYTES (64 MiB) on each GPU it
+ * runs on, held until the process ends.  The first call on a device looks up that
+ * device's copy; no call allocates or frees anything.
+ *   - Shapes whose pieces exceed the array (pa_decode_workspace_bytes(...) above 64 MiB,
+ *     about num_seqs * num_q_heads * ceil(max_context_len / P) * (head_dim + 2) * 4
+ *     bytes) return PA_ERR_SCRATCH before anything is enqueued.
+ *   - Every call writes the pieces it reads, so nothing needs clearing between calls.
+ *     All calls on one GPU share the array: calls that overlap in time on one GPU (two
+ *     streams, two threads, a graph replay beside an eager call) race and give
+ *     undefined results; order them on one stream.
+ * Errors: as pa_decode, with PA_ERR_SCRATCH in place of PA_ERR_WORKSPACE; PA_ERR_HIP if the
+ * scratch's device address cannot be obtained. */
+#define PA_DECODE_NOALLOC_SCRATCH_BYTES (64u << 20)
+pa_status pa_decode_noalloc(const void* q, int32_t q_dtype, int32_t num_seqs, int32_t num_q_heads,
+                            const void* k_cache, const void* v_cache, const pa_kv_cache* cache,
+                            const int32_t* block_tables, int32_t max_blocks_per_seq,
+                            const int32_t* context_lens, int32_t max_context_len, float scale, void* out,
+                            int32_t partition_tokens, int32_t kernel, void* stream);
 
 /* First stage of pa_decode alone (same arguments and checks).  For every
  * sequence with context_lens[b] <= P it writes out[b] directly; for longer

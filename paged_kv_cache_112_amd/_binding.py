@@ -16,14 +16,14 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.environ.get("PA_LIB") or os.path.join(HERE, "libpa.so")
 
 # pa_status
-PA_OK, PA_ERR_NULL, PA_ERR_SHAPE, PA_ERR_DTYPE, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_HIP = range(7)
+PA_OK, PA_ERR_NULL, PA_ERR_SHAPE, PA_ERR_DTYPE, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_HIP, PA_ERR_SCRATCH = range(8)
 # pa_dtype
 PA_F32, PA_BF16, PA_FP8_E4M3, PA_INT8 = 0, 1, 2, 3
 # pa_kernel
 PA_KERNEL_AUTO, PA_KERNEL_VALU, PA_KERNEL_MFMA = 0, 1, 2
 
 EXPORTED = ("pa_write_kv", "pa_copy_blocks", "pa_copy_blocks_layers", "pa_paged_attention", "pa_slot_mapping", "pa_decode", "pa_decode_partition", "pa_merge",
-            "pa_decode_append", "pa_decode_partition_append",
+            "pa_decode_append", "pa_decode_partition_append", "pa_decode_noalloc",
             "pa_decode_workspace_bytes", "pa_default_partition_tokens", "pa_status_str",
             "pa_check_decode_inputs", "pa_check_slots")
 
@@ -70,6 +70,8 @@ def lib() -> ctypes.CDLL:
         L.pa_paged_attention.restype = ctypes.c_int
         L.pa_decode.argtypes = _DECODE_ARGS
         L.pa_decode.restype = ctypes.c_int
+        L.pa_decode_noalloc.argtypes = _DECODE_ARGS[:13] + [_i32, _i32, _vp]
+        L.pa_decode_noalloc.restype = ctypes.c_int
         L.pa_decode_partition.argtypes = _DECODE_ARGS
         L.pa_decode_partition.restype = ctypes.c_int
         L.pa_decode_append.argtypes = _APPEND_ARGS
@@ -137,6 +139,14 @@ def pa_decode(q, q_dtype, num_seqs, num_q_heads, k_cache, v_cache, cache: PaKvCa
     return lib().pa_decode(q, q_dtype, num_seqs, num_q_heads, k_cache, v_cache, ctypes.byref(cache), block_tables,
                            max_blocks_per_seq, context_lens, max_context_len, scale, out, workspace,
                            workspace_bytes, partition_tokens, kernel, stream)
+
+
+def pa_decode_noalloc(q, q_dtype, num_seqs, num_q_heads, k_cache, v_cache, cache: PaKvCache, block_tables,
+                      max_blocks_per_seq, context_lens, max_context_len, scale, out, partition_tokens=0,
+                      kernel=PA_KERNEL_AUTO, stream=None) -> int:
+    return lib().pa_decode_noalloc(q, q_dtype, num_seqs, num_q_heads, k_cache, v_cache, ctypes.byref(cache),
+                                   block_tables, max_blocks_per_seq, context_lens, max_context_len, scale, out,
+                                   partition_tokens, kernel, stream)
 
 
 def pa_decode_partition(q, q_dtype, num_seqs, num_q_heads, k_cache, v_cache, cache: PaKvCache, block_tables,

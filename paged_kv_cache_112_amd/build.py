@@ -17,7 +17,7 @@ LIB_NAME = "libpa.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
 ARCH = "gfx950"
 
-SOURCES = ["api.cpp", "check.cpp", "write_kv.hip", "copy_blocks.hip", "attention_mfma.hip", "step_tensors.hip", "decode_mfma.hip", "decode_valu.hip", "merge.hip"]
+SOURCES = ["api.cpp", "check.cpp", "write_kv.hip", "copy_blocks.hip", "attention_mfma.hip", "step_tensors.hip", "decode_mfma.hip", "decode_valu.hip", "merge.hip", "noalloc.hip"]
 
 # Packed-fp32 instructions are disabled on purpose; fp32 denormals are kept.
 COMMON_FLAGS = [

@@ -6,6 +6,7 @@
 #include <cstdint>
 
 #include "../../include/pa.h"
+#include "api_internal.hpp"
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -187,6 +188,24 @@ pa_status run_merge(const DecodeCall& c, void* stream) {
 }
 
 }  // namespace
+
+pa_status pa::decode_in_scratch(const void* q, int32_t q_dtype, int32_t num_seqs, int32_t num_q_heads,
+                                const void* k_cache, const void* v_cache, const pa_kv_cache* cache,
+                                const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                const int32_t* context_lens, int32_t max_context_len, float scale, void* out,
+                                int32_t partition_tokens, int32_t kernel, uint8_t* scratch, size_t scratch_bytes,
+                                void* stream) {
+  if (!scratch) return PA_ERR_SCRATCH;
+  DecodeCall c;
+  pa_status s = prepare_decode(q, q_dtype, num_seqs, num_q_heads, k_cache, v_cache, cache, block_tables,
+                               max_blocks_per_seq, context_lens, max_context_len, scale, out, scratch, scratch_bytes,
+                               partition_tokens, kernel, &c);
+  if (s == PA_ERR_WORKSPACE) return PA_ERR_SCRATCH;
+  if (s != PA_OK) return s;
+  s = run_partition(c, stream);
+  if (s != PA_OK) return s;
+  return run_merge(c, stream);
+}
 
 extern "C" {
 
@@ -443,6 +462,7 @@ const char* pa_status_str(pa_status s) {
     case PA_ERR_UNSUPPORTED: return "PA_ERR_UNSUPPORTED: unsupported head_dim, block_size, partition or kernel";
     case PA_ERR_WORKSPACE: return "PA_ERR_WORKSPACE: workspace missing or too small";
     case PA_ERR_HIP: return "PA_ERR_HIP: kernel launch failed";
+    case PA_ERR_SCRATCH: return "PA_ERR_SCRATCH: the call needs more than the library's static scratch holds";
   }
   return "unknown pa_status";
 }

@@ -31,7 +31,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_status_strings():
-    for s in range(7):
+    for s in range(8):
         assert pa.status_str(s).startswith("PA_")
     assert pa.pa_default_partition_tokens() == 256
 
