@@ -38,7 +38,7 @@ LAYERS = 8
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_mfma_llama3_8b_b64.traffic.json")
 KERNEL_SOURCES = ["paged_kv_cache_112_amd/csrc/decode_mfma.hip", "paged_kv_cache_112_amd/csrc/common.hpp",
                   "paged_kv_cache_112_amd/csrc/mfma_tiles.hpp", "paged_kv_cache_112_amd/csrc/launch.hpp",
-                  "paged_kv_cache_112_amd/csrc/merge_rows.hpp"]
+                  "paged_kv_cache_112_amd/csrc/merge_rows.hpp", "paged_kv_cache_112_amd/csrc/merge.hip"]
 
 
 def algorithmic_bytes(w, kv_bytes=2, q_bytes=2, out_bytes=2, in_bytes=2):
