@@ -626,8 +626,9 @@ def main():
         return round(float(np.percentile(np.asarray(xs), p)), 2)
 
     # ---- pa_decode alone (partition + merge, the dominant launch): back-to-back graph replays ---
-    def time_decode(tables, layer_pools):
-        g = capture(lambda: [decode(*layer_pools[i], tables) for i in range(LAYERS)])
+    def time_decode(tables, layer_pools, fn=None):
+        fn = fn or decode
+        g = capture(lambda: [fn(*layer_pools[i], tables) for i in range(LAYERS)])
         g.replay()
         torch.cuda.synchronize()
         reps = max(2, args.steps // LAYERS)
@@ -650,6 +651,13 @@ def main():
         return e0.elapsed_time(e1) * 1e3 / (reps * LAYERS), per
 
     decode_us, decode_spread = time_decode(bt, pools)
+
+    # the partition stage alone (pa_decode_partition), as earlier figures quoted it
+    def partition_only(kc, vc, tables=bt):
+        pa.decode_partition(q, kc, vc, tables, ctx, w.scale, out=out, max_context_len=max_ctx, workspace=ws,
+                            partition_tokens=P, kernel=args.kernel, k_scale=k_scale, v_scale=v_scale)
+
+    part_us, _ = time_decode(bt, pools, partition_only)
 
     nb = algorithmic_bytes(w, kv_bytes=1 if fp8 else 2)
     value = nb["step"] / (ms_per_step * 1e-3) / 1e9
@@ -703,6 +711,9 @@ def main():
                             else "pa_write_kv(64 tokens) + pa_decode_partition + pa_merge" if args.two_launch
                             else "pa_write_kv(64 tokens) + pa_decode"),
                    "block_order": "identity (contiguous comparator)" if args.contiguous else "seeded permutation"},
+        "decode_partition": {"us": round(part_us, 2),
+                             "GB/s": round(nb["partition"] / (part_us * 1e-6) / 1e9, 1),
+                             "frac": round(nb["partition"] / (part_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)},
         "pa_decode": {"us": round(decode_us, 2), "us_median": pct(decode_spread, 50),
                       "us_p10": pct(decode_spread, 10), "us_p90": pct(decode_spread, 90),
                       "GB/s": round(achieved, 1), "tokens_per_s": round(B / (decode_us * 1e-6), 1),
