@@ -1,0 +1,29 @@
+"""The C ABI from C: a C99 program built with gcc against include/pa.h, linked to libpa.so.
+
+Checks that the header compiles as plain C (no C++ or torch types in it) and that the
+library links and answers its host-only entry points from a C caller; no GPU is used.
+"""
+import os
+import shutil
+import subprocess
+
+import pytest
+
+import paged_kv_cache_112_amd as pa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.mark.skipif(shutil.which("gcc") is None, reason="gcc not available")
+def test_c_caller(tmp_path):
+    lib = pa.LIB_PATH
+    if not os.path.exists(lib):
+        pytest.skip("libpa.so not built")
+    exe = tmp_path / "abi_smoke"
+    subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-I", os.path.join(ROOT, "include"),
+                    os.path.join(ROOT, "tests", "c", "abi_smoke.c"), "-o", str(exe), lib,
+                    f"-Wl,-rpath,{os.path.dirname(lib)}"], check=True, capture_output=True, text=True)
+    r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=120)
+    print(r.stdout)
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert r.stdout.count("ok ") == 8
