@@ -374,6 +374,28 @@ pa_status pa_check_decode_inputs(const int32_t* block_tables, int32_t max_blocks
 pa_status pa_check_slots(const int32_t* slot_mapping, int32_t num_tokens, int64_t num_blocks, int32_t block_size,
                          int64_t* bad_index);
 
+/* The checked build.  libpa_checked.so is built from the same sources with
+ * -DPA_CHECKED=1: its kernels test what the release kernels trust -- every slot
+ * against num_blocks * block_size (pa_write_kv), every block id a call reads against
+ * [0, num_blocks) (decode, append, multi-query), every context length against its
+ * table (max_blocks_per_seq * block_size) and against max_context_len, and copy ids
+ * against the pool -- and on a breach set a bit in a device error word and go on with a
+ * safe value (the token skipped, block 0 read, the length clipped, the request or pair
+ * skipped), so outputs are then wrong but nothing outside the pools is touched.  The
+ * bits: */
+#define PA_CHECKED_SLOT   1u  /* a slot past the pool */
+#define PA_CHECKED_BLOCK  2u  /* a block id outside the pool */
+#define PA_CHECKED_LENGTH 4u  /* a context past its table or past max_context_len */
+#define PA_CHECKED_PAIR   8u  /* a copy-on-write id past the pool */
+
+/* 1 in the checked build, 0 in the release build. */
+int32_t pa_checked_build(void);
+
+/* Checked build: waits for the current device to finish all its work (a host
+ * synchronization; not for capture in a graph), returns the error bits raised since the
+ * last call in *flags and clears them.  Release build: *flags = 0, PA_ERR_UNSUPPORTED. */
+pa_status pa_checked_errors(uint32_t* flags);
+
 /* Static, human-readable name of a status code. */
 const char* pa_status_str(pa_status status);
 

@@ -25,7 +25,9 @@ PA_KERNEL_AUTO, PA_KERNEL_VALU, PA_KERNEL_MFMA = 0, 1, 2
 EXPORTED = ("pa_write_kv", "pa_copy_blocks", "pa_copy_blocks_layers", "pa_paged_attention", "pa_slot_mapping", "pa_decode", "pa_decode_partition", "pa_merge",
             "pa_decode_append", "pa_decode_partition_append", "pa_decode_noalloc",
             "pa_decode_workspace_bytes", "pa_default_partition_tokens", "pa_status_str",
-            "pa_check_decode_inputs", "pa_check_slots")
+            "pa_check_decode_inputs", "pa_check_slots", "pa_checked_build", "pa_checked_errors")
+# pa_checked_errors bits
+PA_CHECKED_SLOT, PA_CHECKED_BLOCK, PA_CHECKED_LENGTH, PA_CHECKED_PAIR = 1, 2, 4, 8
 
 
 class PaKvCache(ctypes.Structure):
@@ -53,45 +55,55 @@ def lib() -> ctypes.CDLL:
     """The loaded library; raises if ``libpa.so`` has not been built."""
     global _lib
     if _lib is None:
-        if not os.path.exists(LIB_PATH):
-            raise RuntimeError(f"HIP library not built: {LIB_PATH} is missing "
-                               "(run __graft_entry__.build() or python paged_kv_cache_112_amd/build.py)")
-        L = ctypes.CDLL(LIB_PATH)
-        L.pa_write_kv.argtypes = [_vp, _vp, _i32, _i32, _vp, _vp, _vp, ctypes.POINTER(PaKvCache), _vp]
-        L.pa_write_kv.restype = ctypes.c_int
-        L.pa_copy_blocks.argtypes = [_vp, _vp, ctypes.POINTER(PaKvCache), _vp, _vp, _i32, _vp]
-        L.pa_copy_blocks.restype = ctypes.c_int
-        L.pa_copy_blocks_layers.argtypes = [_vp, _vp, ctypes.POINTER(PaKvCache), _i32, _vp, _vp, _i32, _vp]
-        L.pa_copy_blocks_layers.restype = ctypes.c_int
-        L.pa_slot_mapping.argtypes = [_vp, _i32, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp]
-        L.pa_slot_mapping.restype = ctypes.c_int
-        L.pa_paged_attention.argtypes = [_vp, _i32, _i32, _i32, _i32, _vp, _vp, ctypes.POINTER(PaKvCache), _vp,
-                                         _i32, _vp, _vp, _i32, ctypes.c_float, _vp, _vp]
-        L.pa_paged_attention.restype = ctypes.c_int
-        L.pa_decode.argtypes = _DECODE_ARGS
-        L.pa_decode.restype = ctypes.c_int
-        L.pa_decode_noalloc.argtypes = _DECODE_ARGS[:13] + [_i32, _i32, _vp]
-        L.pa_decode_noalloc.restype = ctypes.c_int
-        L.pa_decode_partition.argtypes = _DECODE_ARGS
-        L.pa_decode_partition.restype = ctypes.c_int
-        L.pa_decode_append.argtypes = _APPEND_ARGS
-        L.pa_decode_append.restype = ctypes.c_int
-        L.pa_decode_partition_append.argtypes = _APPEND_ARGS
-        L.pa_decode_partition_append.restype = ctypes.c_int
-        L.pa_merge.argtypes = [_vp, _sz, _i32, _i32, _i32, _vp, _i32, _i32, _i32, _vp, _vp]
-        L.pa_merge.restype = ctypes.c_int
-        L.pa_decode_workspace_bytes.argtypes = [_i32, _i32, _i32, _i32, _i32]
-        L.pa_decode_workspace_bytes.restype = _sz
-        L.pa_default_partition_tokens.argtypes = []
-        L.pa_default_partition_tokens.restype = _i32
-        L.pa_check_decode_inputs.argtypes = [_vp, _i32, _vp, _i32, _i32, _i64, _i32, ctypes.POINTER(_i64)]
-        L.pa_check_decode_inputs.restype = ctypes.c_int
-        L.pa_check_slots.argtypes = [_vp, _i32, _i64, _i32, ctypes.POINTER(_i64)]
-        L.pa_check_slots.restype = ctypes.c_int
-        L.pa_status_str.argtypes = [ctypes.c_int]
-        L.pa_status_str.restype = ctypes.c_char_p
-        _lib = L
+        _lib = load_library(LIB_PATH)
     return _lib
+
+
+def load_library(path: str) -> ctypes.CDLL:
+    """A build of the library at ``path`` (the release or the checked one) with every
+    entry point's argument types set; raises if the file is missing."""
+    if not os.path.exists(path):
+        raise RuntimeError(f"HIP library not built: {path} is missing "
+                           "(run __graft_entry__.build() or python paged_kv_cache_112_amd/build.py)")
+    L = ctypes.CDLL(path)
+    L.pa_write_kv.argtypes = [_vp, _vp, _i32, _i32, _vp, _vp, _vp, ctypes.POINTER(PaKvCache), _vp]
+    L.pa_write_kv.restype = ctypes.c_int
+    L.pa_copy_blocks.argtypes = [_vp, _vp, ctypes.POINTER(PaKvCache), _vp, _vp, _i32, _vp]
+    L.pa_copy_blocks.restype = ctypes.c_int
+    L.pa_copy_blocks_layers.argtypes = [_vp, _vp, ctypes.POINTER(PaKvCache), _i32, _vp, _vp, _i32, _vp]
+    L.pa_copy_blocks_layers.restype = ctypes.c_int
+    L.pa_slot_mapping.argtypes = [_vp, _i32, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp]
+    L.pa_slot_mapping.restype = ctypes.c_int
+    L.pa_paged_attention.argtypes = [_vp, _i32, _i32, _i32, _i32, _vp, _vp, ctypes.POINTER(PaKvCache), _vp,
+                                     _i32, _vp, _vp, _i32, ctypes.c_float, _vp, _vp]
+    L.pa_paged_attention.restype = ctypes.c_int
+    L.pa_decode.argtypes = _DECODE_ARGS
+    L.pa_decode.restype = ctypes.c_int
+    L.pa_decode_noalloc.argtypes = _DECODE_ARGS[:13] + [_i32, _i32, _vp]
+    L.pa_decode_noalloc.restype = ctypes.c_int
+    L.pa_decode_partition.argtypes = _DECODE_ARGS
+    L.pa_decode_partition.restype = ctypes.c_int
+    L.pa_decode_append.argtypes = _APPEND_ARGS
+    L.pa_decode_append.restype = ctypes.c_int
+    L.pa_decode_partition_append.argtypes = _APPEND_ARGS
+    L.pa_decode_partition_append.restype = ctypes.c_int
+    L.pa_merge.argtypes = [_vp, _sz, _i32, _i32, _i32, _vp, _i32, _i32, _i32, _vp, _vp]
+    L.pa_merge.restype = ctypes.c_int
+    L.pa_decode_workspace_bytes.argtypes = [_i32, _i32, _i32, _i32, _i32]
+    L.pa_decode_workspace_bytes.restype = _sz
+    L.pa_default_partition_tokens.argtypes = []
+    L.pa_default_partition_tokens.restype = _i32
+    L.pa_check_decode_inputs.argtypes = [_vp, _i32, _vp, _i32, _i32, _i64, _i32, ctypes.POINTER(_i64)]
+    L.pa_check_decode_inputs.restype = ctypes.c_int
+    L.pa_check_slots.argtypes = [_vp, _i32, _i64, _i32, ctypes.POINTER(_i64)]
+    L.pa_check_slots.restype = ctypes.c_int
+    L.pa_checked_build.argtypes = []
+    L.pa_checked_build.restype = _i32
+    L.pa_checked_errors.argtypes = [ctypes.POINTER(ctypes.c_uint32)]
+    L.pa_checked_errors.restype = ctypes.c_int
+    L.pa_status_str.argtypes = [ctypes.c_int]
+    L.pa_status_str.restype = ctypes.c_char_p
+    return L
 
 
 def status_str(status: int) -> str:

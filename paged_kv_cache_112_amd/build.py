@@ -15,9 +15,11 @@ CSRC = os.path.join(HERE, "csrc")
 ROOT = os.path.dirname(HERE)
 LIB_NAME = "libpa.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
+# the checked build: kernels bounds-check slots, block ids and lengths (-DPA_CHECKED=1)
+CHECKED_LIB_PATH = os.path.join(HERE, "libpa_checked.so")
 ARCH = "gfx950"
 
-SOURCES = ["api.cpp", "check.cpp", "write_kv.hip", "copy_blocks.hip", "attention_mfma.hip", "step_tensors.hip", "decode_mfma.hip", "decode_valu.hip", "merge.hip", "noalloc.hip"]
+SOURCES = ["api.cpp", "check.cpp", "write_kv.hip", "copy_blocks.hip", "attention_mfma.hip", "step_tensors.hip", "decode_mfma.hip", "decode_valu.hip", "merge.hip", "noalloc.hip", "checked.hip"]
 
 # Packed-fp32 instructions are disabled on purpose; fp32 denormals are kept.
 COMMON_FLAGS = [
@@ -52,11 +54,16 @@ def _compile(args):
     return r.stderr
 
 
-def build(verbose: bool = False, extra_flags: list[str] | None = None, out_path: str | None = None) -> str:
-    """Compile every source for gfx950 and link ``libpa.so`` (or ``out_path``); returns its path."""
+def build(verbose: bool = False, extra_flags: list[str] | None = None, out_path: str | None = None,
+          checked: bool = False) -> str:
+    """Compile every source for gfx950 and link ``libpa.so`` (``libpa_checked.so`` with
+    ``checked``, or ``out_path``); returns its path."""
     cc = hipcc()
-    lib_path = out_path or LIB_PATH
-    obj_dir = os.path.join(HERE, "_build") if out_path is None else lib_path + ".objs"
+    lib_path = out_path or (CHECKED_LIB_PATH if checked else LIB_PATH)
+    if checked:
+        extra_flags = list(extra_flags or []) + ["-DPA_CHECKED=1"]
+    obj_dir = (os.path.join(HERE, "_build_checked" if checked else "_build") if out_path is None
+               else lib_path + ".objs")
     os.makedirs(obj_dir, exist_ok=True)
     flags = COMMON_FLAGS + list(extra_flags or [])
     jobs, objs = [], []
@@ -80,3 +87,4 @@ def build(verbose: bool = False, extra_flags: list[str] | None = None, out_path:
 
 if __name__ == "__main__":
     print(build(verbose=True))
+    print(build(verbose=True, checked=True))

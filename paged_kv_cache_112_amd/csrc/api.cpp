@@ -156,6 +156,8 @@ pa_status prepare_decode(const void* q, int32_t q_dtype, int32_t num_seqs, int32
   a.k_cache_w = nullptr;
   a.v_cache_w = nullptr;
   a.inv_k = a.inv_v = 1.0f;
+  a.num_blocks = cache->num_blocks;
+  a.err = pa::checked_error_word();
   call->kernel = k;
   call->ws = ws;
   return PA_OK;
@@ -246,6 +248,8 @@ pa_status pa_write_kv(const void* k, const void* v, int32_t in_dtype, int32_t nu
   a.mode = mode;
   a.inv_k = is_scaled(cache->dtype) ? 1.0f / cache->k_scale : 1.0f;
   a.inv_v = is_scaled(cache->dtype) ? 1.0f / cache->v_scale : 1.0f;
+  a.num_slots = cache->num_blocks * (int64_t)cache->block_size;
+  a.err = pa::checked_error_word();
   return pa::launch_write_kv(a, static_cast<hipStream_t>(stream)) == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 
@@ -271,6 +275,7 @@ pa_status pa_copy_blocks_layers(void* k_cache, void* v_cache, const pa_kv_cache*
   a.layer_bytes = a.block_bytes * cache->num_blocks;
   a.num_pairs = num_pairs;
   a.num_layers = num_layers;
+  a.err = pa::checked_error_word();
   return pa::launch_copy_blocks(a, static_cast<hipStream_t>(stream)) == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 
@@ -315,6 +320,8 @@ pa_status pa_paged_attention(const void* q, int32_t q_dtype, int32_t num_tokens,
   const float ks = is_scaled(cache->dtype) ? cache->k_scale : 1.0f;
   a.qk_scale = scale * kLog2e * ks;
   a.v_scale = is_scaled(cache->dtype) ? cache->v_scale : 1.0f;
+  a.num_blocks = cache->num_blocks;
+  a.err = pa::checked_error_word();
   const int64_t per_wg = pa::attention_tokens_per_workgroup(a.log2_group);
   if (((int64_t)max_query_len + per_wg - 1) / per_wg * a.num_kv_heads > INT32_MAX) return PA_ERR_SHAPE;
   return pa::launch_attention_mfma(a, static_cast<hipStream_t>(stream)) == hipSuccess ? PA_OK : PA_ERR_HIP;

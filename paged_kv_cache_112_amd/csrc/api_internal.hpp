@@ -16,4 +16,8 @@ pa_status decode_in_scratch(const void* q, int32_t q_dtype, int32_t num_seqs, in
                             int32_t max_context_len, float scale, void* out, int32_t partition_tokens,
                             int32_t kernel, uint8_t* scratch, size_t scratch_bytes, void* stream);
 
+// The checked build's device error word on the current device (nullptr in a release
+// build, or when it cannot be found).
+uint32_t* checked_error_word();
+
 }  // namespace pa

@@ -90,6 +90,12 @@ __global__ __launch_bounds__(256) void attention_mfma_kernel(const AttnArgs a) {
   const int t0 = ((blockIdx.x / a.num_kv_heads) * kAttnWaves + wave) * (NQ * T);
   // past this request's queries, or inconsistent lengths (uniform per wave; no barrier follows)
   if (t0 >= nq || nq > S || q0 < 0 || q0 + nq > a.num_tokens) return;
+  if constexpr (kChecked) {                // a context past its table: reported, the request skipped
+    if ((int64_t)S > (int64_t)a.bt_stride * a.block_size) {
+      flag_error(a.err, kErrLength);
+      return;
+    }
+  }
 
   const int lane = threadIdx.x & 63;
   const int G = 1 << a.log2_group;
@@ -147,10 +153,10 @@ __global__ __launch_bounds__(256) void attention_mfma_kernel(const AttnArgs a) {
   auto row_ptr = [&](const uint8_t* base, int r, int tile, uint32_t lane_bytes) -> const uint8_t* {
     const int tc = min(16 * tile + r, S - 1);
     if constexpr (BIGBS) {
-      const int32_t blk = attn_load_uniform(bt_row + (min(16 * tile, S - 1) >> a.log2_bs));
+      const int32_t blk = checked_block(attn_load_uniform(bt_row + (min(16 * tile, S - 1) >> a.log2_bs)), a.num_blocks, a.err);
       return base + (int64_t)blk * a.block_bytes + (size_t)((uint32_t)(tc & bs_mask) * row_bytes + lane_bytes);
     } else {
-      const int32_t blk = bt_row[tc >> a.log2_bs];
+      const int32_t blk = checked_block(bt_row[tc >> a.log2_bs], a.num_blocks, a.err);
       return base + (int64_t)blk * a.block_bytes + (size_t)((uint32_t)(tc & bs_mask) * row_bytes + lane_bytes);
     }
   };
@@ -167,7 +173,8 @@ __global__ __launch_bounds__(256) void attention_mfma_kernel(const AttnArgs a) {
   auto load_ids = [&](int st, int32_t (&id)[2]) {
     if (step_fast(st)) {
 #pragma unroll
-      for (int h = 0; h < 2; ++h) id[h] = attn_load_uniform(bt_row + ((32 * st + 16 * h) >> a.log2_bs));
+      for (int h = 0; h < 2; ++h)
+        id[h] = checked_block(attn_load_uniform(bt_row + ((32 * st + 16 * h) >> a.log2_bs)), a.num_blocks, a.err);
     }
   };
   auto step_addr = [&](int st, const int32_t (&id)[2]) {

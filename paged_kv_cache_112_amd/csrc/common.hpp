@@ -4,7 +4,27 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "launch.hpp"
+
 namespace pa {
+
+// Checked build: record a broken contract in the device error word (a vector atomic OR).
+__device__ __forceinline__ void flag_error(uint32_t* err, uint32_t bit) {
+  if constexpr (kChecked) {
+    if (err != nullptr) atomicOr(err, bit);
+  }
+}
+
+// Checked build: a block id outside [0, num_blocks) is reported and replaced by block 0.
+__device__ __forceinline__ int32_t checked_block(int32_t blk, int64_t num_blocks, uint32_t* err) {
+  if constexpr (kChecked) {
+    if (blk < 0 || (int64_t)blk >= num_blocks) {
+      flag_error(err, kErrBlock);
+      return 0;
+    }
+  }
+  return blk;
+}
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));

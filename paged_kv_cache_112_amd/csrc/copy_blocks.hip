@@ -27,7 +27,12 @@ __global__ __launch_bounds__(kCopyThreads) void copy_blocks_kernel(const CopyArg
   const int32_t s = a.src[blockIdx.y];
   const int32_t d = a.dst[blockIdx.y];
   // ids outside the pool (negative padding included) are skipped
-  if (s < 0 || d < 0 || (int64_t)s >= a.num_blocks || (int64_t)d >= a.num_blocks) return;
+  if (s < 0 || d < 0 || (int64_t)s >= a.num_blocks || (int64_t)d >= a.num_blocks) {
+    // negative ids are padding; an id past the pool is reported in the checked build
+    if ((int64_t)s >= a.num_blocks || (int64_t)d >= a.num_blocks)
+      if (threadIdx.x == 0 && blockIdx.x == 0 && blockIdx.z == 0) flag_error(a.err, kErrPair);
+    return;
+  }
   const int64_t layer_off = (int64_t)blockIdx.z * a.layer_bytes;
   const int64_t src_off = layer_off + (int64_t)s * a.block_bytes;
   const int64_t dst_off = layer_off + (int64_t)d * a.block_bytes;

@@ -91,7 +91,7 @@ __device__ __forceinline__ void append_token(const DecodeArgs& a, int b, int kvh
   if (lane >= 2 * CH) return;
   const bool is_v = lane >= CH;
   const int c = is_v ? lane - CH : lane;
-  const int32_t blk = a.block_tables[(int64_t)b * a.bt_stride + (pos >> a.log2_bs)];
+  const int32_t blk = checked_block(a.block_tables[(int64_t)b * a.bt_stride + (pos >> a.log2_bs)], a.num_blocks, a.err);
   const int64_t row = (int64_t)blk * a.block_size + (pos & (a.block_size - 1));
   const u32x4 x = ld16((is_v ? a.v_new : a.k_new) + ((int64_t)b * a.num_kv_heads + kvh) * D + 8 * c);
   uint8_t* dst = (is_v ? a.v_cache_w : a.k_cache_w) + row * a.row_bytes + (int64_t)(kvh * D + 8 * c) * ESZ;
@@ -144,6 +144,16 @@ void decode_mfma_kernel(const DecodeArgs a) {
     if (part * P >= ctx && !(part == 0 && ctx == 0)) return;
   }
   const int t0 = part * P;          // same for the whole workgroup
+  if constexpr (kChecked) {
+    // a context past its table would read entries beyond the row: reported and clipped
+    if ((int64_t)ctx > (int64_t)a.max_parts * P) flag_error(a.err, kErrLength);
+    const int64_t cap = (int64_t)a.bt_stride * a.block_size;
+    if ((int64_t)ctx > cap) {
+      flag_error(a.err, kErrLength);
+      ctx = (int)cap;
+      if (t0 >= ctx) return;                                     // uniform over the workgroup
+    }
+  }
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
@@ -180,7 +190,7 @@ void decode_mfma_kernel(const DecodeArgs a) {
     // blocks shorter than a tile: stage the partition's table entries in LDS
     const int n_tok = min(P, ctx - t0);
     const int n_ent = ((t0 + n_tok - 1) >> a.log2_bs) - lb0 + 1;
-    for (int i = threadIdx.x; i < n_ent; i += blockDim.x) tbl[i] = bt_row[i];
+    for (int i = threadIdx.x; i < n_ent; i += blockDim.x) tbl[i] = checked_block(bt_row[i], a.num_blocks, a.err);
     __syncthreads();
   }
 
@@ -197,7 +207,9 @@ void decode_mfma_kernel(const DecodeArgs a) {
   int32_t tile_blk[BIGBS ? PT : 1];
   if constexpr (BIGBS) {
 #pragma unroll
-    for (int i = 0; i < PT; ++i) tile_blk[i] = load_uniform(bt_row + ((min(t0 + 16 * (i * W + w), ctx - 1) >> log2bs) - lb0));
+    for (int i = 0; i < PT; ++i)
+      tile_blk[i] = checked_block(load_uniform(bt_row + ((min(t0 + 16 * (i * W + w), ctx - 1) >> log2bs) - lb0)),
+                                  a.num_blocks, a.err);
   }
   auto tile_block = [&](int i) -> int64_t { return (int64_t)tile_blk[i] * block_bytes; };
   auto row_off = [&](int t) -> int64_t {

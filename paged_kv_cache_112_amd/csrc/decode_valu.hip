@@ -83,6 +83,16 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(const DecodeArgs a) {
     if (part * P >= ctx && !(part == 0 && ctx == 0)) return;
   }
   const int t0 = part * P;
+  if constexpr (kChecked) {
+    // a context past its table would read entries beyond the row: reported and clipped
+    if ((int64_t)ctx > (int64_t)a.max_parts * P) flag_error(a.err, kErrLength);
+    const int64_t cap = (int64_t)a.bt_stride * a.block_size;
+    if ((int64_t)ctx > cap) {
+      flag_error(a.err, kErrLength);
+      ctx = (int)cap;
+      if (t0 >= ctx) return;                                     // uniform over the workgroup
+    }
+  }
 
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
@@ -107,7 +117,7 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(const DecodeArgs a) {
   const int lb0 = t0 >> a.log2_bs;
   const int n_ent = ((t0 + n_tok - 1) >> a.log2_bs) - lb0 + 1;
   const int32_t* bt_row = a.block_tables + (int64_t)b * a.bt_stride + lb0;
-  for (int i = threadIdx.x; i < n_ent; i += blockDim.x) tbl[i] = bt_row[i];
+  for (int i = threadIdx.x; i < n_ent; i += blockDim.x) tbl[i] = checked_block(bt_row[i], a.num_blocks, a.err);
   __syncthreads();
 
   const int64_t head_off = (int64_t)kvh * D * ESZ + (int64_t)d0 * ESZ;

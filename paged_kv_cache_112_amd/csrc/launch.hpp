@@ -6,6 +6,17 @@
 
 namespace pa {
 
+// The checked build (-DPA_CHECKED=1): kernels test the block ids, slots and context lengths
+// they are handed against the pool and the tables, count a breach in a device error word
+// (the kErr* bits) and go on with a safe value (block 0, a skipped row, a clipped length),
+// so a broken caller contract is reported instead of reading or writing outside the pools.
+// The release build compiles none of it.
+#ifndef PA_CHECKED
+#define PA_CHECKED 0
+#endif
+constexpr bool kChecked = PA_CHECKED != 0;
+enum : uint32_t { kErrSlot = 1u, kErrBlock = 2u, kErrLength = 4u, kErrPair = 8u };
+
 struct WriteArgs {
   const void* k;
   const void* v;
@@ -16,6 +27,8 @@ struct WriteArgs {
   int32_t row_elems;   // H_kv * head_dim
   int32_t mode;        // 0 bf16 copy, 1 f32 copy, 2 bf16 -> e4m3, 3 f32 -> e4m3, 4 bf16 -> int8, 5 f32 -> int8
   float inv_k, inv_v;  // fp32(1 / scale) for e4m3 and int8 pools
+  int64_t num_slots;   // num_blocks * block_size (checked build)
+  uint32_t* err;       // device error word (checked build; nullptr otherwise)
 };
 
 // Storage formats, numbered as pa_dtype in include/pa.h.
@@ -48,6 +61,8 @@ struct DecodeArgs {
   uint8_t* k_cache_w;        // the pools, writable (same addresses as k_cache, v_cache)
   uint8_t* v_cache_w;
   float inv_k, inv_v;        // fp32(1 / scale) for one-byte pools
+  int64_t num_blocks;        // checked build: the pool's block count
+  uint32_t* err;             // checked build: device error word (nullptr otherwise)
 };
 
 // Launches with at most this many partitions per sequence merge with one 16-lane row per
@@ -92,6 +107,7 @@ struct CopyArgs {
   int64_t layer_bytes;       // multi-layer pools: distance between layers' pools (0 for one layer)
   int32_t num_pairs;
   int32_t num_layers;
+  uint32_t* err;             // checked build: device error word (nullptr otherwise)
 };
 
 struct AttnArgs {
@@ -107,6 +123,8 @@ struct AttnArgs {
   int32_t block_size, log2_bs, bt_stride, max_query_len;
   int32_t num_kv_heads, kv_fmt;
   float qk_scale, v_scale;
+  int64_t num_blocks;        // checked build: the pool's block count
+  uint32_t* err;             // checked build: device error word (nullptr otherwise)
 };
 
 struct SlotArgs {

@@ -20,12 +20,19 @@ template <WriteMode M>
 __global__ __launch_bounds__(128) void write_kv_kernel(const uint8_t* __restrict__ k, const uint8_t* __restrict__ v,
                                                        const int32_t* __restrict__ slots, uint8_t* __restrict__ kc,
                                                        uint8_t* __restrict__ vc, int64_t total_chunks,
-                                                       int32_t chunks_per_row, float inv_k, float inv_v) {
+                                                       int32_t chunks_per_row, float inv_k, float inv_v,
+                                                       int64_t num_slots, uint32_t* err) {
   const int64_t item = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (item >= total_chunks) return;
   const int64_t tok = item / chunks_per_row;
   const int32_t c = (int32_t)(item - tok * chunks_per_row);
   const int32_t slot = slots[tok];
+  if constexpr (kChecked) {                  // a slot past the pool: reported, the token skipped
+    if (slot >= num_slots) {
+      if (c == 0) flag_error(err, kErrSlot);
+      return;
+    }
+  }
   const int64_t src_elem = item * 8;                                   // == tok * row + c * 8
   const int64_t dst_elem = (int64_t)slot * chunks_per_row * 8 + (int64_t)c * 8;
   if constexpr (M == WriteMode::kCopy16) {                             // bf16 -> bf16
@@ -95,17 +102,17 @@ hipError_t launch_write_kv(const WriteArgs& a, hipStream_t stream) {
   uint8_t* vc = static_cast<uint8_t*>(a.v_cache);
   switch (a.mode) {
     case 0: hipLaunchKernelGGL(write_kv_kernel<WriteMode::kCopy16>, grid, block, 0, stream, k, v, a.slots, kc, vc,
-                               total, cpr, a.inv_k, a.inv_v); break;
+                               total, cpr, a.inv_k, a.inv_v, a.num_slots, a.err); break;
     case 1: hipLaunchKernelGGL(write_kv_kernel<WriteMode::kCopy32>, grid, block, 0, stream, k, v, a.slots, kc, vc,
-                               total, cpr, a.inv_k, a.inv_v); break;
+                               total, cpr, a.inv_k, a.inv_v, a.num_slots, a.err); break;
     case 2: hipLaunchKernelGGL(write_kv_kernel<WriteMode::kBf16ToE4m3>, grid, block, 0, stream, k, v, a.slots, kc,
-                               vc, total, cpr, a.inv_k, a.inv_v); break;
+                               vc, total, cpr, a.inv_k, a.inv_v, a.num_slots, a.err); break;
     case 3: hipLaunchKernelGGL(write_kv_kernel<WriteMode::kF32ToE4m3>, grid, block, 0, stream, k, v, a.slots, kc,
-                               vc, total, cpr, a.inv_k, a.inv_v); break;
+                               vc, total, cpr, a.inv_k, a.inv_v, a.num_slots, a.err); break;
     case 4: hipLaunchKernelGGL(write_kv_kernel<WriteMode::kBf16ToInt8>, grid, block, 0, stream, k, v, a.slots, kc,
-                               vc, total, cpr, a.inv_k, a.inv_v); break;
+                               vc, total, cpr, a.inv_k, a.inv_v, a.num_slots, a.err); break;
     default: hipLaunchKernelGGL(write_kv_kernel<WriteMode::kF32ToInt8>, grid, block, 0, stream, k, v, a.slots, kc,
-                                vc, total, cpr, a.inv_k, a.inv_v); break;
+                                vc, total, cpr, a.inv_k, a.inv_v, a.num_slots, a.err); break;
   }
   return hipGetLastError();
 }
