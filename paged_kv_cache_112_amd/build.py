@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(HERE, LIB_NAME)
 CHECKED_LIB_PATH = os.path.join(HERE, "libpa_checked.so")
 ARCH = "gfx950"
 
-SOURCES = ["api.cpp", "check.cpp", "write_kv.hip", "copy_blocks.hip", "attention_mfma.hip", "step_tensors.hip", "decode_mfma.hip", "decode_valu.hip", "merge.hip", "noalloc.hip", "checked.hip"]
+SOURCES = ["api.cpp", "check.cpp", "write_kv.hip", "copy_blocks.hip", "attention_mfma.hip", "attention_lds.hip", "step_tensors.hip", "decode_mfma.hip", "decode_valu.hip", "merge.hip", "noalloc.hip", "checked.hip"]
 
 # Packed-fp32 instructions are disabled on purpose; fp32 denormals are kept.
 COMMON_FLAGS = [
@@ -36,6 +36,7 @@ COMMON_FLAGS = [
 # register files at each loop iteration.
 SOURCE_FLAGS = {
     "attention_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "attention_lds.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 }
 
 

@@ -21,6 +21,10 @@ constexpr size_t kAlign = 256;
 #ifndef PA_MAX_HEADS_PER_WG
 #define PA_MAX_HEADS_PER_WG 4
 #endif
+// multi-query attention: shapes the LDS-sharing kernel covers use it
+#ifndef PA_ATTN_LDS
+#define PA_ATTN_LDS 1
+#endif
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
@@ -322,9 +326,12 @@ pa_status pa_paged_attention(const void* q, int32_t q_dtype, int32_t num_tokens,
   a.v_scale = is_scaled(cache->dtype) ? cache->v_scale : 1.0f;
   a.num_blocks = cache->num_blocks;
   a.err = pa::checked_error_word();
-  const int64_t per_wg = pa::attention_tokens_per_workgroup(a.log2_group);
+  const bool lds = PA_ATTN_LDS && pa::attention_lds_supported(a);
+  const int64_t per_wg = lds ? pa::attention_lds_tokens_per_workgroup(a.log2_group)
+                             : pa::attention_tokens_per_workgroup(a.log2_group);
   if (((int64_t)max_query_len + per_wg - 1) / per_wg * a.num_kv_heads > INT32_MAX) return PA_ERR_SHAPE;
-  return pa::launch_attention_mfma(a, static_cast<hipStream_t>(stream)) == hipSuccess ? PA_OK : PA_ERR_HIP;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  return (lds ? pa::launch_attention_lds(a, s) : pa::launch_attention_mfma(a, s)) == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 
 pa_status pa_slot_mapping(const int32_t* block_tables, int32_t max_blocks_per_seq, int32_t* seq_lens,

@@ -140,6 +140,11 @@ hipError_t launch_slot_mapping(const SlotArgs& a, hipStream_t stream);
 hipError_t launch_attention_mfma(const AttnArgs& a, hipStream_t stream);
 // new tokens of one request handled by one workgroup of the multi-query kernel
 int attention_tokens_per_workgroup(int log2_group);
+// the multi-query kernel with K/V tiles shared through LDS (bf16 pools, head_dim 128,
+// blocks of 16 tokens or more)
+bool attention_lds_supported(const AttnArgs& a);
+int attention_lds_tokens_per_workgroup(int log2_group);
+hipError_t launch_attention_lds(const AttnArgs& a, hipStream_t stream);
 hipError_t launch_copy_blocks(const CopyArgs& a, hipStream_t stream);
 hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_decode_valu(const DecodeArgs& a, hipStream_t stream);

@@ -85,6 +85,18 @@ def test_mixed_query_lengths(hq, hkv, d, bs):
     assert np.abs(out_to_f64(m.run(scale)) - m.oracle(scale)).max() <= 2e-2
 
 
+@pytest.mark.parametrize("hq,hkv", [(16, 8), (32, 4)])
+@pytest.mark.parametrize("bs", [16, 32])
+def test_bf16_head128_group_sizes(hq, hkv, bs):
+    """bf16 pools at head_dim 128 with blocks of 16 tokens or more (the kernel that shares K/V
+    tiles through LDS): group sizes 2 and 8, which the shapes above leave to head_dim 64."""
+    seq_lens = [1, 5, 40, 300, 17, 130, 64, 333]
+    qlens = [1, 5, 40, 300, 16, 17, 1, 129]
+    m = MQ(seq_lens, qlens, hq, hkv, 128, bs, seed=hq + bs)
+    scale = float(np.float32(1 / np.sqrt(128)))
+    assert np.abs(out_to_f64(m.run(scale)) - m.oracle(scale)).max() <= 2e-2
+
+
 @pytest.mark.parametrize("kv", ["e4m3", "i8"])
 @pytest.mark.parametrize("hq,hkv,d,bs", [(16, 8, 64, 16), (32, 2, 128, 4), (8, 8, 64, 64), (32, 4, 64, 1)])
 def test_one_byte_pools_across_shapes(kv, hq, hkv, d, bs):
@@ -121,15 +133,16 @@ def test_scores_growing_along_the_context(kv):
     assert np.abs(out_to_f64(m.run(scale)) - m.oracle(scale)).max() <= 2e-2
 
 
+@pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("B", [63, 64, 65, 130])
-def test_many_requests(B):
+def test_many_requests(B, d):
     """Up to 64 requests are ranked longest first inside the kernel, beyond that taken in order:
-    both sides of the limit, with lengths that tie."""
+    both sides of the limit, with lengths that tie (head_dim 128 runs the LDS-sharing kernel)."""
     rng = np.random.default_rng(B)
     seq_lens = rng.integers(1, 200, B)
     seq_lens[::9] = 96                                # ties
     qlens = np.minimum(seq_lens, rng.integers(0, 40, B))
-    m = MQ(seq_lens, qlens, 16, 4, 64, 16, seed=B)
+    m = MQ(seq_lens, qlens, 16, 4, d, 16, seed=B)
     scale = 0.125
     assert np.abs(out_to_f64(m.run(scale)) - m.oracle(scale)).max() <= 2e-2
 
@@ -150,11 +163,12 @@ def test_one_token_per_sequence_matches_decode():
     assert np.abs(out_to_f64(dec) - ref).max() <= 2e-2
 
 
-def test_sequences_with_no_new_tokens_and_bad_lengths_are_skipped():
+@pytest.mark.parametrize("d", [64, 128])
+def test_sequences_with_no_new_tokens_and_bad_lengths_are_skipped(d):
     """A sequence with no rows writes nothing; one claiming more new tokens than its context is skipped."""
     import torch
     import paged_kv_cache_112_amd as pa
-    m = MQ([40, 12, 30], [4, 0, 6], 16, 4, 64, 16, seed=5)
+    m = MQ([40, 12, 30], [4, 0, 6], 16, 4, d, 16, seed=5)
     scale = 0.125
     ref = m.oracle(scale)
     out = m.run(scale)
