@@ -1,6 +1,6 @@
 // Multi-query paged attention (chunked prefill, or several new tokens per sequence),
-// matrix-core path with the K/V tiles shared through LDS: bf16 q on a bf16 pool,
-// head_dim 128, blocks of 16 tokens or more.
+// matrix-core path with the K/V tiles shared through LDS: bf16 q on a bf16, e4m3 or
+// int8 pool, head_dim 128, blocks of 16 tokens or more.
 //
 // What is computed is what attention_mfma.hip computes: request i's n_i new tokens are
 // the last positions of its context of S_i tokens, new token j attends causally to
@@ -16,6 +16,10 @@
 // (two staging sets, even and odd steps) and stores them to the other half of a
 // double-buffered LDS tile at the end of the step before they are used, so a wave
 // holds no K or V beyond the operands of one product and two waves fit on each SIMD.
+// One-byte pools (e4m3, int8) are widened to bf16 exactly as the rows go to LDS (every
+// e4m3 and int8 value is a bf16 value; the pool's scales are applied to the scores and
+// the output), so each element is widened once per workgroup and everything after the
+// store is the bf16 kernel.
 //   * q.K^T: v_mfma_f32_16x16x32_bf16, A = 16 keys x 32 head dimensions read from LDS
 //     (ds_read_b128; a row's 16-byte segments are XOR-swizzled with the row so the 16
 //     rows of an operand hit distinct banks), B = q^T held in registers.
@@ -46,10 +50,11 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const uint8_t* lds, uint32_t off)
   return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4bf16(p));
 }
 
-template <int NQ>
+template <int KF, int NQ>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attention_lds_kernel(const AttnArgs a) {
   constexpr int D = 128;
+  constexpr int ESZ = byte_fmt(KF) ? 1 : 2;   // pool bytes per element
   constexpr int NKK = D / 32;        // 32-dimension slices of q.K^T
   constexpr int NE = D / 16;         // 16-dimension blocks of P.V
   constexpr int ROWB = D * 2;        // bytes of one key row of one KV head
@@ -107,8 +112,8 @@ void attention_lds_kernel(const AttnArgs a) {
 
   // ---- cooperative staging: thread (key, segment) of the step's 32 rows ----------
   const int32_t* bt_row = a.block_tables + (int64_t)i * a.bt_stride;
-  const uint8_t* kbase = a.k_cache + (int64_t)kvh * ROWB;
-  const uint8_t* vbase = a.v_cache + (int64_t)kvh * ROWB;
+  const uint8_t* kbase = a.k_cache + (int64_t)kvh * D * ESZ;
+  const uint8_t* vbase = a.v_cache + (int64_t)kvh * D * ESZ;
   const int bs_mask = a.block_size - 1;
   const uint32_t row_bytes = (uint32_t)a.row_bytes;
   const int skey = threadIdx.x >> 4, sseg = threadIdx.x & 15;
@@ -202,23 +207,35 @@ void attention_lds_kernel(const AttnArgs a) {
   // Set 0 holds the even steps' segments, set 1 the odd ones'.  idn: block ids of the
   // next step to request.  Each 16-key tile lies in one block; a tile past the context
   // takes the block of its last row, and rows clamp to the context.
-  u32x4 rk0, rv0, rk1, rv1;
+  // a segment is 8 elements of one row: 16 bytes of a bf16 pool, 8 of a one-byte pool
+  typedef typename std::conditional<byte_fmt(KF), u32x2, u32x4>::type Seg;
+  Seg rk0, rv0, rk1, rv1;
   int32_t idn[2];
   auto load_ids = [&](int st, int32_t (&id)[2]) {
 #pragma unroll
     for (int h = 0; h < 2; ++h)
       id[h] = checked_block(attn_load_uniform(bt_row + (min(32 * st + 16 * h, S - 1) >> a.log2_bs)), a.num_blocks, a.err);
   };
-  auto fetch2 = [&](int st, const int32_t (&id)[2], u32x4& xk, u32x4& xv) {
+  auto fetch2 = [&](int st, const int32_t (&id)[2], Seg& xk, Seg& xv) {
     const int tc = min(32 * st + skey, S - 1);
     const int32_t blk = (skey >> 4) ? id[1] : id[0];
-    const int64_t off = (int64_t)blk * a.block_bytes + (int64_t)((uint32_t)(tc & bs_mask) * row_bytes + 16 * sseg);
-    xk = ld16(kbase + off);
-    xv = ld16(vbase + off);
+    constexpr uint32_t SEGB = sizeof(Seg);
+    const int64_t off = (int64_t)blk * a.block_bytes + (int64_t)((uint32_t)(tc & bs_mask) * row_bytes + SEGB * sseg);
+    xk = *reinterpret_cast<const Seg*>(kbase + off);
+    xv = *reinterpret_cast<const Seg*>(vbase + off);
   };
-  auto put2 = [&](int buf, const u32x4& xk, const u32x4& xv) {
-    *reinterpret_cast<u32x4*>(&lk[buf][k_st]) = xk;
-    *reinterpret_cast<u32x4*>(&lv[buf][v_st]) = xv;
+  // 8 elements as bf16 (one-byte formats widened exactly)
+  auto widen = [&](const Seg& x) -> u32x4 {
+    if constexpr (!byte_fmt(KF)) {
+      return x;
+    } else {
+      return u32x4{bytes2_to_bf16x2<KF, false>(x[0]), bytes2_to_bf16x2<KF, true>(x[0]),
+                   bytes2_to_bf16x2<KF, false>(x[1]), bytes2_to_bf16x2<KF, true>(x[1])};
+    }
+  };
+  auto put2 = [&](int buf, const Seg& xk, const Seg& xv) {
+    *reinterpret_cast<u32x4*>(&lk[buf][k_st]) = widen(xk);
+    *reinterpret_cast<u32x4*>(&lv[buf][v_st]) = widen(xv);
   };
   {
     int32_t id[2];
@@ -280,7 +297,7 @@ void attention_lds_kernel(const AttnArgs a) {
 constexpr int kLdsNq = PA_ATTN_LDS_NQ;
 
 bool attention_lds_supported(const AttnArgs& a) {
-  return a.kv_fmt == kBf16 && a.head_dim == 128 && a.block_size >= 16;
+  return (a.kv_fmt == kBf16 || a.kv_fmt == kE4m3 || a.kv_fmt == kInt8) && a.head_dim == 128 && a.block_size >= 16;
 }
 
 int attention_lds_tokens_per_workgroup(int log2_group) { return kLdsWaves * kLdsNq * (16 >> log2_group); }
@@ -290,7 +307,12 @@ hipError_t launch_attention_lds(const AttnArgs& a, hipStream_t s) {
   const int per_wg = attention_lds_tokens_per_workgroup(a.log2_group);
   const int wgs = (a.max_query_len + per_wg - 1) / per_wg;
   const dim3 grid((unsigned)(wgs * a.num_kv_heads), (unsigned)a.num_seqs);
-  hipLaunchKernelGGL((attention_lds_kernel<kLdsNq>), grid, dim3(kWave * kLdsWaves), 0, s, a);
+  const dim3 block(kWave * kLdsWaves);
+  switch (a.kv_fmt) {
+    case kBf16: hipLaunchKernelGGL((attention_lds_kernel<kFmtBf16, kLdsNq>), grid, block, 0, s, a); break;
+    case kE4m3: hipLaunchKernelGGL((attention_lds_kernel<kFmtE4m3, kLdsNq>), grid, block, 0, s, a); break;
+    default: hipLaunchKernelGGL((attention_lds_kernel<kFmtInt8, kLdsNq>), grid, block, 0, s, a); break;
+  }
   return hipGetLastError();
 }
 

@@ -85,14 +85,15 @@ def test_mixed_query_lengths(hq, hkv, d, bs):
     assert np.abs(out_to_f64(m.run(scale)) - m.oracle(scale)).max() <= 2e-2
 
 
-@pytest.mark.parametrize("hq,hkv", [(16, 8), (32, 4)])
+@pytest.mark.parametrize("kv", ["bf16", "e4m3", "i8"])
+@pytest.mark.parametrize("hq,hkv", [(16, 8), (32, 4), (16, 16), (32, 2)])
 @pytest.mark.parametrize("bs", [16, 32])
-def test_bf16_head128_group_sizes(hq, hkv, bs):
-    """bf16 pools at head_dim 128 with blocks of 16 tokens or more (the kernel that shares K/V
-    tiles through LDS): group sizes 2 and 8, which the shapes above leave to head_dim 64."""
+def test_head128_group_sizes(kv, hq, hkv, bs):
+    """head_dim 128 with blocks of 16 tokens or more (the kernel that shares K/V tiles through
+    LDS, one-byte pools widened as they go to LDS): group sizes 2, 8, 1 and 16."""
     seq_lens = [1, 5, 40, 300, 17, 130, 64, 333]
     qlens = [1, 5, 40, 300, 16, 17, 1, 129]
-    m = MQ(seq_lens, qlens, hq, hkv, 128, bs, seed=hq + bs)
+    m = MQ(seq_lens, qlens, hq, hkv, 128, bs, kv, seed=hq + bs)
     scale = float(np.float32(1 / np.sqrt(128)))
     assert np.abs(out_to_f64(m.run(scale)) - m.oracle(scale)).max() <= 2e-2
 
