@@ -371,11 +371,17 @@ def test_partition_pieces_match_oracle(kv, kernel, P):
 
 
 @pytest.mark.parametrize("out_fmt", ["f32", "bf16"])
-def test_merge_matches_oracle(out_fmt):
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("jmax", [12, 32, 60, 128, 300])
+def test_merge_matches_oracle(out_fmt, D, jmax):
+    """Both merge schedules: the row merge (up to 16 partitions) and the four-wave merge with
+    2, 4 and 8 partitions per group and batch (32 or fewer, 64, more; 300 takes three
+    batches, the last partial), over sequences of 2, 3, 7, up to 17 and jmax partitions
+    (one partition is finished by the partition kernel and never merged)."""
     import torch
     import paged_kv_cache_112_amd as pa
-    B, H, D, P = 5, 6, 128, 32
-    ctx = np.array([33, 64, 65, 200, 1000], dtype=np.int32)
+    B, H, P = 6, 6, 32
+    ctx = np.array([40, 33, 65, 200, min(530, jmax * P - 5), jmax * P - 5], dtype=np.int32)
     J = -(-int(ctx.max()) // P)
     rng = np.random.default_rng(41)
     m = (rng.standard_normal((B, H, J)) * 4).astype(np.float32)
