@@ -539,7 +539,10 @@ def main():
     ctx = to_dev(w.context_lens)
     max_ctx = int(w.context_lens.max())
     out = torch.empty((B, hq, d), dtype=torch.bfloat16, device=dev)
-    P = args.partition or pa.pa_default_partition_tokens()
+    # the partition size pa_decode takes by itself on the matrix cores (passed explicitly,
+    # so that the two-launch and partition-only figures use the same one)
+    P = args.partition or (pa.pa_default_partition_tokens() if args.kernel == pa.PA_KERNEL_VALU
+                           else pa.pa_partition_tokens_for(max_ctx))
     ws = pa.new_workspace(B, hq, d, max_ctx, P, dev)
     if ws is None:
         ws = torch.empty(1, dtype=torch.uint8, device=dev)

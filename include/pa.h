@@ -146,8 +146,19 @@ pa_status pa_copy_blocks(void* k_cache, void* v_cache, const pa_kv_cache* cache,
 pa_status pa_copy_blocks_layers(void* k_cache, void* v_cache, const pa_kv_cache* cache, int32_t num_layers,
                                 const int32_t* src, const int32_t* dst, int32_t num_pairs, void* stream);
 
-/* Partition size (tokens) used when a call passes partition_tokens = 0. */
+/* Partition size (tokens) used when a call passes partition_tokens = 0: 256, except that
+ * the whole-decode calls (pa_decode, pa_decode_append, pa_decode_noalloc) on the
+ * matrix-core path take pa_partition_tokens_for(max_context_len).  The two-stage calls
+ * (pa_decode_partition, pa_decode_partition_append, pa_merge) and
+ * pa_decode_workspace_bytes always take 256 for 0, so that a merge finds the pieces its
+ * partition launch wrote; a workspace sized for 256 also holds the pieces of any larger
+ * partition size. */
 int32_t pa_default_partition_tokens(void);
+
+/* The partition size a whole decode on the matrix cores takes for partition_tokens = 0:
+ * 512 tokens when max_context_len >= 4096 (half the split-K partial outputs), else 256.
+ * Host-only; no error. */
+int32_t pa_partition_tokens_for(int32_t max_context_len);
 
 /* Workspace bytes pa_decode / pa_decode_partition / pa_merge need for this shape
  * (0 when max_context_len fits in one partition).  partition_tokens = 0 means the

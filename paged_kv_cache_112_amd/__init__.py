@@ -9,5 +9,5 @@ from ._binding import (  # noqa: F401
     PaKvCache, cache_desc, check, check_decode_inputs, check_slots, copy_blocks, decode, decode_append, decode_partition, decode_partition_append,
     paged_attention, slot_mapping, decode_workspace_bytes, dtype_code, lib, merge,
     pa_copy_blocks, pa_copy_blocks_layers, pa_paged_attention, pa_slot_mapping, pa_decode, pa_decode_append, pa_decode_noalloc,
-    pa_decode_partition, pa_decode_partition_append, pa_decode_workspace_bytes, pa_default_partition_tokens, pa_merge,
+    pa_decode_partition, pa_decode_partition_append, pa_decode_workspace_bytes, pa_default_partition_tokens, pa_merge, pa_partition_tokens_for,
     pa_write_kv, status_str, workspace_views, write_kv, new_workspace)

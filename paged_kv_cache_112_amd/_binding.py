@@ -24,7 +24,7 @@ PA_KERNEL_AUTO, PA_KERNEL_VALU, PA_KERNEL_MFMA = 0, 1, 2
 
 EXPORTED = ("pa_write_kv", "pa_copy_blocks", "pa_copy_blocks_layers", "pa_paged_attention", "pa_slot_mapping", "pa_decode", "pa_decode_partition", "pa_merge",
             "pa_decode_append", "pa_decode_partition_append", "pa_decode_noalloc",
-            "pa_decode_workspace_bytes", "pa_default_partition_tokens", "pa_status_str",
+            "pa_decode_workspace_bytes", "pa_default_partition_tokens", "pa_partition_tokens_for", "pa_status_str",
             "pa_check_decode_inputs", "pa_check_slots", "pa_checked_build", "pa_checked_errors")
 # pa_checked_errors bits
 PA_CHECKED_SLOT, PA_CHECKED_BLOCK, PA_CHECKED_LENGTH, PA_CHECKED_PAIR = 1, 2, 4, 8
@@ -93,6 +93,8 @@ def load_library(path: str) -> ctypes.CDLL:
     L.pa_decode_workspace_bytes.restype = _sz
     L.pa_default_partition_tokens.argtypes = []
     L.pa_default_partition_tokens.restype = _i32
+    L.pa_partition_tokens_for.argtypes = [_i32]
+    L.pa_partition_tokens_for.restype = _i32
     L.pa_check_decode_inputs.argtypes = [_vp, _i32, _vp, _i32, _i32, _i64, _i32, ctypes.POINTER(_i64)]
     L.pa_check_decode_inputs.restype = ctypes.c_int
     L.pa_check_slots.argtypes = [_vp, _i32, _i64, _i32, ctypes.POINTER(_i64)]
@@ -198,6 +200,10 @@ def pa_decode_workspace_bytes(num_seqs, num_q_heads, head_dim, max_context_len, 
 
 def pa_default_partition_tokens() -> int:
     return lib().pa_default_partition_tokens()
+
+
+def pa_partition_tokens_for(max_context_len: int) -> int:
+    return lib().pa_partition_tokens_for(int(max_context_len))
 
 
 def _host_i32(a):

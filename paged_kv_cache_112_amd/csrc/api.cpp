@@ -13,6 +13,11 @@
 namespace {
 
 constexpr int32_t kDefaultPartition = 256;
+// The single-call decodes on the matrix-core path take 512-token partitions from this
+// context length on (half the partial outputs; measured faster on 8192- and
+// 32768-token batches, slower on batches of 3,360-token contexts).
+constexpr int32_t kLongContext = 4096;
+constexpr int32_t kLongPartition = 512;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr size_t kAlign = 256;
 #ifndef PA_MAX_WG_WAVES
@@ -92,7 +97,7 @@ pa_status prepare_decode(const void* q, int32_t q_dtype, int32_t num_seqs, int32
                          const int32_t* block_tables, int32_t max_blocks_per_seq,
                          const int32_t* context_lens, int32_t max_context_len, float scale, void* out,
                          void* workspace, size_t workspace_bytes, int32_t partition_tokens, int32_t kernel,
-                         DecodeCall* call) {
+                         bool whole_call, DecodeCall* call) {
   if (!q || !k_cache || !v_cache || !cache || !block_tables || !context_lens || !out) return PA_ERR_NULL;
   if (const pa_status s = check_cache(cache); s != PA_OK) return s;
   if (num_seqs < 0 || num_q_heads < 1 || max_blocks_per_seq < 1 || max_context_len < 0) return PA_ERR_SHAPE;
@@ -104,11 +109,15 @@ pa_status prepare_decode(const void* q, int32_t q_dtype, int32_t num_seqs, int32
   const bool bf16_q = q_dtype == PA_BF16 && cache->dtype != PA_F32;
   if (!f32_pair && !bf16_q) return PA_ERR_DTYPE;
   const int32_t group = num_q_heads / cache->num_kv_heads;
-  const int32_t P = partition_tokens == 0 ? kDefaultPartition : partition_tokens;
-  if (!valid_partition(P)) return PA_ERR_UNSUPPORTED;
   if (kernel < PA_KERNEL_AUTO || kernel > PA_KERNEL_MFMA) return PA_ERR_UNSUPPORTED;
   int32_t k = kernel;
   if (k == PA_KERNEL_AUTO) k = f32_pair ? PA_KERNEL_VALU : PA_KERNEL_MFMA;
+  // partition_tokens = 0: the two-stage calls (whose pa_merge cannot know the kernel) and
+  // the vector path take 256 tokens; a whole decode on the matrix cores takes the size
+  // pa_partition_tokens_for gives
+  int32_t P = partition_tokens;
+  if (P == 0) P = whole_call && k == PA_KERNEL_MFMA ? pa_partition_tokens_for(max_context_len) : kDefaultPartition;
+  if (!valid_partition(P)) return PA_ERR_UNSUPPORTED;
   if (k == PA_KERNEL_MFMA && (f32_pair || group > 16)) return PA_ERR_UNSUPPORTED;
   if (k == PA_KERNEL_VALU && group > 8) return PA_ERR_UNSUPPORTED;
   // partitions beyond 256 tokens: matrix-core grid kernel only (several waves per KV head)
@@ -205,7 +214,7 @@ pa_status pa::decode_in_scratch(const void* q, int32_t q_dtype, int32_t num_seqs
   DecodeCall c;
   pa_status s = prepare_decode(q, q_dtype, num_seqs, num_q_heads, k_cache, v_cache, cache, block_tables,
                                max_blocks_per_seq, context_lens, max_context_len, scale, out, scratch, scratch_bytes,
-                               partition_tokens, kernel, &c);
+                               partition_tokens, kernel, true, &c);
   if (s == PA_ERR_WORKSPACE) return PA_ERR_SCRATCH;
   if (s != PA_OK) return s;
   s = run_partition(c, stream);
@@ -216,6 +225,10 @@ pa_status pa::decode_in_scratch(const void* q, int32_t q_dtype, int32_t num_seqs
 extern "C" {
 
 int32_t pa_default_partition_tokens(void) { return kDefaultPartition; }
+
+int32_t pa_partition_tokens_for(int32_t max_context_len) {
+  return max_context_len >= kLongContext ? kLongPartition : kDefaultPartition;
+}
 
 size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim, int32_t max_context_len,
                                  int32_t partition_tokens) {
@@ -365,7 +378,7 @@ pa_status pa_decode_partition(const void* q, int32_t q_dtype, int32_t num_seqs, 
   DecodeCall c;
   const pa_status s = prepare_decode(q, q_dtype, num_seqs, num_q_heads, k_cache, v_cache, cache, block_tables,
                                      max_blocks_per_seq, context_lens, max_context_len, scale, out, workspace,
-                                     workspace_bytes, partition_tokens, kernel, &c);
+                                     workspace_bytes, partition_tokens, kernel, false, &c);
   if (s != PA_OK) return s;
   return run_partition(c, stream);
 }
@@ -375,11 +388,12 @@ static pa_status prepare_append(const void* q, int32_t q_dtype, const void* k_ne
                                 int32_t num_seqs, int32_t num_q_heads, void* k_cache, void* v_cache,
                                 const pa_kv_cache* cache, const int32_t* block_tables, int32_t max_blocks_per_seq,
                                 const int32_t* context_lens, int32_t max_context_len, float scale, void* out,
-                                void* workspace, size_t workspace_bytes, int32_t partition_tokens, DecodeCall* c) {
+                                void* workspace, size_t workspace_bytes, int32_t partition_tokens, bool whole_call,
+                                DecodeCall* c) {
   if (!k_new || !v_new) return PA_ERR_NULL;
   const pa_status s = prepare_decode(q, q_dtype, num_seqs, num_q_heads, k_cache, v_cache, cache, block_tables,
                                      max_blocks_per_seq, context_lens, max_context_len, scale, out, workspace,
-                                     workspace_bytes, partition_tokens, PA_KERNEL_MFMA, c);
+                                     workspace_bytes, partition_tokens, PA_KERNEL_MFMA, whole_call, c);
   if (s != PA_OK) return s;
   if (in_dtype != PA_BF16) return PA_ERR_DTYPE;
   if (c->args.partition_tokens < 256) return PA_ERR_UNSUPPORTED;
@@ -402,7 +416,7 @@ pa_status pa_decode_partition_append(const void* q, int32_t q_dtype, const void*
   DecodeCall c;
   const pa_status s = prepare_append(q, q_dtype, k_new, v_new, in_dtype, num_seqs, num_q_heads, k_cache, v_cache,
                                      cache, block_tables, max_blocks_per_seq, context_lens, max_context_len, scale,
-                                     out, workspace, workspace_bytes, partition_tokens, &c);
+                                     out, workspace, workspace_bytes, partition_tokens, false, &c);
   if (s != PA_OK) return s;
   return run_partition(c, stream);
 }
@@ -415,7 +429,7 @@ pa_status pa_decode_append(const void* q, int32_t q_dtype, const void* k_new, co
   DecodeCall c;
   pa_status s = prepare_append(q, q_dtype, k_new, v_new, in_dtype, num_seqs, num_q_heads, k_cache, v_cache, cache,
                                block_tables, max_blocks_per_seq, context_lens, max_context_len, scale, out,
-                               workspace, workspace_bytes, partition_tokens, &c);
+                               workspace, workspace_bytes, partition_tokens, true, &c);
   if (s != PA_OK) return s;
   s = run_partition(c, stream);
   if (s != PA_OK) return s;
@@ -430,7 +444,7 @@ pa_status pa_decode(const void* q, int32_t q_dtype, int32_t num_seqs, int32_t nu
   DecodeCall c;
   pa_status s = prepare_decode(q, q_dtype, num_seqs, num_q_heads, k_cache, v_cache, cache, block_tables,
                                max_blocks_per_seq, context_lens, max_context_len, scale, out, workspace,
-                               workspace_bytes, partition_tokens, kernel, &c);
+                               workspace_bytes, partition_tokens, kernel, true, &c);
   if (s != PA_OK) return s;
   s = run_partition(c, stream);
   if (s != PA_OK) return s;

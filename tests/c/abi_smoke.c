@@ -21,6 +21,7 @@ int main(void) {
   const size_t want = 2 * ((rows * 4 + 255) / 256 * 256) + (rows * 128 * 4 + 255) / 256 * 256;
   CHECK(pa_decode_workspace_bytes(64, 32, 128, 3360, 0) == want, "workspace bytes");
   CHECK(pa_default_partition_tokens() == 256, "default partition");
+  CHECK(pa_partition_tokens_for(4095) == 256 && pa_partition_tokens_for(4096) == 512, "partition for long contexts");
   CHECK(pa_status_str(PA_ERR_SHAPE)[0] == 'P', "status string");
 
   pa_kv_cache cache = {64, 16, 2, 64, PA_BF16, 1.0f, 1.0f};

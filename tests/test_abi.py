@@ -34,6 +34,7 @@ def test_status_strings():
     for s in range(8):
         assert pa.status_str(s).startswith("PA_")
     assert pa.pa_default_partition_tokens() == 256
+    assert [pa.pa_partition_tokens_for(n) for n in (0, 1, 4095, 4096, 8192, 1 << 20)] == [256, 256, 256, 512, 512, 512]
 
 
 def test_workspace_bytes():

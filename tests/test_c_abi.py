@@ -26,4 +26,4 @@ def test_c_caller(tmp_path):
     r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=120)
     print(r.stdout)
     assert r.returncode == 0, r.stdout + r.stderr
-    assert r.stdout.count("ok ") == 8
+    assert r.stdout.count("ok ") == 9
