@@ -1,5 +1,7 @@
 // Multi-query paged attention (chunked prefill, or several new tokens per sequence),
-// matrix-core path: bf16 q with a bf16, e4m3 or int8 pool.
+// matrix-core path with K/V tiles held in registers: bf16 q with a bf16, e4m3 or int8
+// pool.  It serves the shapes the LDS-sharing kernel (attention_lds.hip) does not:
+// head_dim 64, and blocks of fewer than 16 tokens.
 //
 // What is computed: request i's new tokens are q[qsl[i] .. qsl[i+1]), the last
 // n_i = qsl[i+1] - qsl[i] positions of its context of S_i = seq_lens[i] tokens; new
