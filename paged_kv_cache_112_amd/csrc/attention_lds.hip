@@ -13,9 +13,10 @@
 // heads of the KV head: the 16 columns of one MFMA operand).  Keys advance 32 per step.
 // Each step's K and V rows (2 x 8 KiB) are fetched once for the workgroup: every
 // thread loads one 16-byte segment of K and one of V two steps ahead into registers
-// (two staging sets, even and odd steps) and stores them to the other half of a
-// double-buffered LDS tile at the end of the step before they are used, so a wave
-// holds no K or V beyond the operands of one product and two waves fit on each SIMD.
+// (two staging sets, even and odd steps) and stores them to a ring of four LDS tiles;
+// the waves compute two steps between barriers and store the next two at the end of
+// the pair, so a wave holds no K or V beyond the operands of one product, two waves fit
+// on each SIMD, and the workgroup meets once per 64 keys.
 // One-byte pools (e4m3, int8) are widened to bf16 exactly as the rows go to LDS (every
 // e4m3 and int8 value is a bf16 value; the pool's scales are applied to the scores and
 // the output), so each element is widened once per workgroup and everything after the
@@ -59,8 +60,8 @@ void attention_lds_kernel(const AttnArgs a) {
   constexpr int NE = D / 16;         // 16-dimension blocks of P.V
   constexpr int ROWB = D * 2;        // bytes of one key row of one KV head
   constexpr int TILEB = 32 * ROWB;   // one step's K (or V) rows
-  __shared__ __attribute__((aligned(16))) uint8_t lk[2][TILEB];
-  __shared__ __attribute__((aligned(16))) uint8_t lv[2][TILEB];
+  __shared__ __attribute__((aligned(16))) uint8_t lk[4][TILEB];
+  __shared__ __attribute__((aligned(16))) uint8_t lv[4][TILEB];
 
   const int kvh = blockIdx.x % a.num_kv_heads;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -89,7 +90,6 @@ void attention_lds_kernel(const AttnArgs a) {
   const int base = S - nq;                           // context position of new token 0
   const int t0 = t0w + wave * NQ * T;                // this wave's first new token
   const int nst_wg = (base + min(t0w + per_wg, nq) + 31) >> 5;
-  const int nfull = (base + t0 + 1) >> 5;            // steps every column of the wave sees whole
   const float sc = a.qk_scale == 0.f ? 1.f : fabsf(a.qk_scale);
   const uint32_t qflip = a.qk_scale < 0.f ? 0x80008000u : 0u;
   const bool qzero = a.qk_scale == 0.f;
@@ -136,6 +136,7 @@ void attention_lds_kernel(const AttnArgs a) {
   const int trk = 4 * q4 + (n >> 2);        // key of this lane's transposing-read row
   const bool active = t0 < nq;               // uniform per wave
   const int nst = active ? (base + min(t0 + NQ * T, nq) + 31) >> 5 : 0;   // this wave's steps
+  const int nfull = active ? (base + t0 + 1) >> 5 : 0;   // steps every column of the wave sees whole
   // One step for every query group of the wave: q.K^T (K from LDS buffer `buf`), the mask
   // when MASKED, the online softmax and O += P.V (V from the same buffer).
   auto compute = [&](auto masked_tag, int st, int buf) {
@@ -243,37 +244,49 @@ void attention_lds_kernel(const AttnArgs a) {
     fetch2(0, id, rk0, rv0);
     load_ids(1, id);
     fetch2(1, id, rk1, rv1);
-    // step 1's loads stay ahead of step 2's, the order the loop keeps, so that each
-    // store in the loop waits only for its own set
     __builtin_amdgcn_sched_barrier(0);
     put2(0, rk0, rv0);
     load_ids(2, id);
     fetch2(2, id, rk0, rv0);
-    load_ids(3, idn);
+    // each set's loads stay in the order the loop keeps, so that a store waits only for
+    // its own set
+    __builtin_amdgcn_sched_barrier(0);
+    put2(1, rk1, rv1);
+    load_ids(3, id);
+    fetch2(3, id, rk1, rv1);
+    load_ids(4, idn);
   }
   __syncthreads();
-  // Step st computes from LDS buffer st % 2 while step st + 1 waits in its staging set;
-  // at its end that set goes to the other buffer and is refilled with step st + 3.  The
-  // staging is unconditional, also for the (at most three) steps past the last: a fixed
-  // count of loads in flight lets each store wait only for its own set.  The loop is
-  // unrolled by two so that both sets keep fixed registers.
+  // Steps st and st + 1 compute from LDS tiles st % 4 and (st + 1) % 4 with no barrier
+  // between them; then steps st + 2 and st + 3 go from the staging sets to the other two
+  // tiles (last read before the previous barrier), the sets are refilled with steps st + 4
+  // and st + 5, and the workgroup meets once.  The staging is unconditional, also for the
+  // (at most seven) steps past the last: a fixed count of loads in flight lets each store
+  // wait only for its own set.  The loop is unrolled by two pairs so that every tile index
+  // is a constant.
   auto run = [&](int st, int buf) {
     if (st < nfull) compute(std::false_type{}, st, buf);
     else if (st < nst) compute(std::true_type{}, st, buf);
   };
-  for (int st = 0;;) {
+  for (int st = 0; st < nst_wg; st += 4) {
     run(st, 0);
-    put2(1, rk1, rv1);
-    fetch2(st + 3, idn, rk1, rv1);
-    load_ids(st + 4, idn);
+    run(st + 1, 1);
+    put2(2, rk0, rv0);
+    fetch2(st + 4, idn, rk0, rv0);
+    load_ids(st + 5, idn);
+    put2(3, rk1, rv1);
+    fetch2(st + 5, idn, rk1, rv1);
+    load_ids(st + 6, idn);
     __syncthreads();
-    if (++st >= nst_wg) break;
-    run(st, 1);
+    run(st + 2, 2);
+    run(st + 3, 3);
     put2(0, rk0, rv0);
-    fetch2(st + 3, idn, rk0, rv0);
-    load_ids(st + 4, idn);
+    fetch2(st + 6, idn, rk0, rv0);
+    load_ids(st + 7, idn);
+    put2(1, rk1, rv1);
+    fetch2(st + 7, idn, rk1, rv1);
+    load_ids(st + 8, idn);
     __syncthreads();
-    if (++st >= nst_wg) break;
   }
   if (!active) return;
 
