@@ -137,10 +137,13 @@ void attention_lds_kernel(const AttnArgs a) {
   const bool active = t0 < nq;               // uniform per wave
   const int nst = active ? (base + min(t0 + NQ * T, nq) + 31) >> 5 : 0;   // this wave's steps
   const int nfull = active ? (base + t0 + 1) >> 5 : 0;   // steps every column of the wave sees whole
-  // One step for every query group of the wave: q.K^T (K from LDS buffer `buf`), the mask
-  // when MASKED, the online softmax and O += P.V (V from the same buffer).
-  auto compute = [&](auto masked_tag, int st, int buf) {
-    constexpr bool MASKED = decltype(masked_tag)::value;
+  // One step for every query group of the wave: q.K^T (K from LDS tile `buf`), the causal
+  // mask on the steps that reach past a column's position, the online softmax and
+  // O += P.V (V from the same tile).  Masked and unmasked steps share this one body, the
+  // mask being a uniform branch around the comparisons alone: with a copy of the body per
+  // case the compiler moved the accumulators to other registers on one path and copied
+  // them back at every step.
+  auto compute = [&](int st, int buf) {
     const uint8_t* kt = lk[buf];
     const uint8_t* vt = lv[buf];
     bf16x8 kop[2][NKK];
@@ -158,7 +161,7 @@ void attention_lds_kernel(const AttnArgs a) {
         s[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[0][kk], qreg[c][kk], s[0], 0, 0, 0);
         s[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[1][kk], qreg[c][kk], s[1], 0, 0, 0);
       }
-      if constexpr (MASKED) {
+      if (st >= nfull) {                          // uniform: a step on the causal diagonal
 #pragma unroll
         for (int h = 0; h < 2; ++h)
 #pragma unroll
@@ -265,8 +268,7 @@ void attention_lds_kernel(const AttnArgs a) {
   // wait only for its own set.  The loop is unrolled by two pairs so that every tile index
   // is a constant.
   auto run = [&](int st, int buf) {
-    if (st < nfull) compute(std::false_type{}, st, buf);
-    else if (st < nst) compute(std::true_type{}, st, buf);
+    if (st < nst) compute(st, buf);
   };
   for (int st = 0; st < nst_wg; st += 4) {
     run(st, 0);
