@@ -65,6 +65,11 @@ def load_library(path: str) -> ctypes.CDLL:
     if not os.path.exists(path):
         raise RuntimeError(f"HIP library not built: {path} is missing "
                            "(run __graft_entry__.build() or python paged_kv_cache_112_amd/build.py)")
+    # torch brings its own HIP runtime, which it asks for by the file name libamdhip64.so.
+    # Loaded after it, this library's libamdhip64.so.7 resolves to that same runtime by its
+    # soname; loaded first, it would bring up the system runtime and torch a second one, and
+    # kernels launched here on torch's memory and streams would fail.
+    import torch  # noqa: F401
     L = ctypes.CDLL(path)
     L.pa_write_kv.argtypes = [_vp, _vp, _i32, _i32, _vp, _vp, _vp, ctypes.POINTER(PaKvCache), _vp]
     L.pa_write_kv.restype = ctypes.c_int

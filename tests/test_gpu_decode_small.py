@@ -212,6 +212,23 @@ def test_decode_equals_its_two_stages_bitwise(P, ctx_extra, kv):
     assert np.abs(out_to_f64(a) - h.oracle_decode()).max() <= TOL[kv]
 
 
+@pytest.mark.parametrize("kv", ["bf16", "e4m3"])
+@pytest.mark.parametrize("longest,expect", [(4095, 256), (4096, 512)])
+def test_default_partition_follows_the_longest_context(kv, longest, expect):
+    """A whole decode on the matrix cores asked for partition_tokens = 0 takes the size
+    pa_partition_tokens_for gives for its max_context_len (256 below 4096 tokens, 512 from
+    there): bit for bit the explicit request, and within tolerance of the oracle."""
+    import paged_kv_cache_112_amd as pa
+    assert pa.pa_partition_tokens_for(longest) == expect
+    w = custom_workload([longest, 1000, 17, 3000, 513], 32, 8, 128, 16, kv, "bf16", seed=longest)
+    dev = DeviceInputs(build_host_inputs(w))
+    assert dev.max_ctx == longest
+    auto = from_dev(dev.decode(partition_tokens=0, kernel=2))
+    explicit = from_dev(dev.decode(partition_tokens=expect, kernel=2))
+    assert np.array_equal(auto, explicit)
+    _check(dev, w, partition_tokens=0, kernel=2)
+
+
 @pytest.mark.parametrize("P", [64, 256])
 def test_repeated_calls_on_one_workspace(P):
     """Calls on one workspace, with the contexts changing between them (as a decode loop's do):
