@@ -277,6 +277,12 @@ def _ptr(t) -> int:
         raise ValueError("expected a device tensor")
     if not t.is_contiguous():
         raise ValueError("expected a contiguous tensor")
+    # the library launches on the current device: a pointer into another GPU's memory would
+    # be read by kernels running on this one
+    cur = _torch().cuda.current_device()
+    if t.device.index is not None and t.device.index != cur:
+        raise ValueError(f"tensor on cuda:{t.device.index} but the current device is cuda:{cur} "
+                         "(call under torch.cuda.device(...))")
     return t.data_ptr()
 
 

@@ -30,3 +30,29 @@ def test_one_hip_runtime_when_the_library_is_loaded_before_torch():
     assert r.returncode == 0, r.stderr[-2000:]
     count = int(r.stdout.split()[0])
     assert count == 1, r.stdout
+
+
+class _FakeDeviceTensor:
+    """Stands in for a contiguous device tensor on another GPU (none exists on this host)."""
+
+    is_cuda = True
+
+    def __init__(self, index):
+        import types
+        self.device = types.SimpleNamespace(index=index)
+
+    def is_contiguous(self):
+        return True
+
+    def data_ptr(self):
+        return 0x1000
+
+
+def test_tensor_on_another_device_is_refused(monkeypatch):
+    import pytest
+    import torch
+    from paged_kv_cache_112_amd import _binding
+    monkeypatch.setattr(torch.cuda, "current_device", lambda: 0)
+    assert _binding._ptr(_FakeDeviceTensor(0)) == 0x1000
+    with pytest.raises(ValueError, match="current device"):
+        _binding._ptr(_FakeDeviceTensor(1))
