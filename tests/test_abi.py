@@ -73,6 +73,7 @@ def _decode(**kw):
     (dict(num_q_heads=5), pa.PA_ERR_SHAPE),                              # H_q % H_kv != 0
     (dict(max_context_len=13 * 16 + 1), pa.PA_ERR_SHAPE),               # beyond the table
     (dict(num_seqs=-1), pa.PA_ERR_SHAPE),
+    (dict(num_seqs=65536), pa.PA_ERR_UNSUPPORTED),                     # past the grid's y limit
     (dict(scale=float("nan")), pa.PA_ERR_SHAPE),
     (dict(q_dtype=pa.PA_BF16), pa.PA_ERR_DTYPE),                        # bf16 q with an f32 pool
     (dict(cache=_cache(head_dim=96)), pa.PA_ERR_UNSUPPORTED),

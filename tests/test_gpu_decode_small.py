@@ -212,6 +212,16 @@ def test_decode_equals_its_two_stages_bitwise(P, ctx_extra, kv):
     assert np.abs(out_to_f64(a) - h.oracle_decode()).max() <= TOL[kv]
 
 
+@pytest.mark.parametrize("kernel", [1, 2])
+def test_the_largest_accepted_batch(kernel):
+    """65,535 sequences (the most pa_decode accepts: the grid's second dimension) of 1 to 8
+    tokens, on both partition kernels: every output row against the oracle."""
+    rng = np.random.default_rng(3)
+    ctx = rng.integers(1, 9, 65535).tolist()
+    w = custom_workload(ctx, 4, 1, 64, 16, "bf16", "bf16", seed=9)
+    _check(DeviceInputs(build_host_inputs(w)), w, partition_tokens=0, kernel=kernel)
+
+
 @pytest.mark.parametrize("kv", ["bf16", "e4m3"])
 @pytest.mark.parametrize("longest,expect", [(4095, 256), (4096, 512)])
 def test_default_partition_follows_the_longest_context(kv, longest, expect):
