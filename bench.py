@@ -34,6 +34,7 @@ sys.path.insert(0, ROOT)
 
 WORKLOAD = "llama3_8b_b64"
 HBM_PEAK_GBS = 8000.0
+MALL_BYTES = 256 << 20          # MI355X memory-side cache (Infinity Cache)
 LAYERS = 8
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_mfma_llama3_8b_b64.traffic.json")
 KERNEL_SOURCES = ["paged_kv_cache_112_amd/csrc/decode_mfma.hip", "paged_kv_cache_112_amd/csrc/common.hpp",
@@ -269,8 +270,14 @@ def side_op(args, w, torch, pa):
             us = _time_launches(torch, lambda: call(src, dst), reps, warm)
             nbytes = 2 * 2 * n * block_bytes                  # K and V, read and written
             gbs = nbytes / us / 1e3
-            lines.append({"pairs": n, "us_per_call": round(us, 2), "bytes": nbytes, "GB/s": round(gbs, 1),
-                          "frac_of_8TBps": round(gbs / HBM_PEAK_GBS, 4)})
+            line = {"pairs": n, "us_per_call": round(us, 2), "bytes": nbytes, "GB/s": round(gbs, 1),
+                    "frac_of_8TBps": round(gbs / HBM_PEAK_GBS, 4)}
+            if nbytes // 2 < 2 * MALL_BYTES:
+                # the written blocks land in the memory-side cache and are drained to HBM while
+                # later calls run: the time is mostly the reads'
+                line["note"] = (f"writes {nbytes // 2 / 1e6:.0f} MB per call, which the 256 MB MALL absorbs "
+                                "between back-to-back calls: not an HBM rate")
+            lines.append(line)
         print(json.dumps({"metric": "pa_copy_blocks (copy-on-write block copies)", "workload": w.name,
                           "block_bytes": block_bytes, "dtype": w.kv_dtype, "results": lines,
                           "timing": "HIP events around back-to-back calls"}))
