@@ -443,6 +443,9 @@ def main():
     ap.add_argument("--workload", default=WORKLOAD,
                     choices=["llama3_8b_b64", "llama3_8b_long", "llama2_7b_mha", "llama3_8b_fp8_prefix"])
     ap.add_argument("--block-size", type=int, default=None, help="block size for llama2_7b_mha")
+    ap.add_argument("--tp", type=int, default=1, metavar="N",
+                    help="one rank's share of the layer under N-way tensor parallelism over KV heads "
+                         "(H_q / N query and H_kv / N KV heads, the same sequences and tables)")
     ap.add_argument("--kv-dtype", default=None, choices=["bf16", "e4m3", "i8"],
                     help="pool format other than the workload's own (same lengths and tables)")
     ap.add_argument("--copy-calibrate", type=int, default=0, metavar="MIB",
@@ -493,6 +496,12 @@ def main():
     w = make_config(args.workload, args.block_size) if args.workload == "llama2_7b_mha" else make_config(args.workload)
     if args.kv_dtype and args.kv_dtype != w.kv_dtype:
         w = w.with_dtypes(args.kv_dtype, "bf16", name=f"{w.name}-{args.kv_dtype}")
+    if args.tp > 1:
+        if w.num_kv_heads % args.tp:
+            raise SystemExit(f"--tp {args.tp} does not divide the {w.num_kv_heads} KV heads")
+        from dataclasses import replace
+        w = replace(w, num_q_heads=w.num_q_heads // args.tp, num_kv_heads=w.num_kv_heads // args.tp,
+                    name=f"{w.name}-tp{args.tp}-rank")
     if args.contiguous:
         from workloads import deal_tables
         w.block_tables, _ = deal_tables(w.context_lens, w.block_size, np.arange(w.num_blocks, dtype=np.int32))
