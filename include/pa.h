@@ -23,6 +23,11 @@
  *     calls, except pa_decode_noalloc's static scratch array (64 MiB on each GPU
  *     the library's code is loaded on); calls are thread-safe, bar the overlap
  *     rule of pa_decode_noalloc.
+ *   - The library links libamdhip64.so.7.  In a process that also runs torch, whose
+ *     wheel ships its own HIP runtime under the file name libamdhip64.so, load torch
+ *     first: this library then binds to that runtime by its soname; loaded first, it
+ *     brings up a second runtime, and its launches on torch's memory and streams fail
+ *     (the Python binding imports torch before it loads the library).
  *   - `stream` is a hipStream_t (NULL = the null stream).  Calls only enqueue
  *     work: no host synchronization, no allocation, so they can be captured in
  *     a HIP graph.
